@@ -1,0 +1,173 @@
+/*
+ * sfkv.h -- C ABI of the streaming FP8 ring KV cache for MI355X (gfx950).
+ *
+ * One cache serves one attention call site of a batch-size-one autoregressive
+ * video diffusion transformer. The operations follow the Runway Characters
+ * research post ("Runway Characters: Serving a 57B Video Diffusion Transformer
+ * for Real-Time Conversation"):
+ *   - "Where the Time Went": every call owns its cache (5,788 slots, 757 new
+ *     per step in production), and the launch software redid RoPE, FP8
+ *     quantisation and a copy-shift of the window over the whole cache on
+ *     every call;
+ *   - "Do It Once, at Write Time": RoPE and FP8 quantisation with per-head
+ *     scales (calibrated once per session) are applied to each new frame as it
+ *     enters the cache; the cache is a ring; a position reset every 42 steps is
+ *     one delta rotation of the cached window; positions follow time order, not
+ *     slot order, once the ring wraps;
+ *   - "What Broke in Production": no host synchronisation in the per-step path
+ *     (a single device-to-host read per step was the worst regression) and no
+ *     buffers keyed by token count.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are plain HIP device addresses; the caller allocates all
+ *     device memory (inputs, outputs, cache storage, workspaces) and keeps it
+ *     alive until the enqueued work has finished. The library never calls
+ *     hipMalloc or hipFree.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     compute call is asynchronous on that stream and never reads device
+ *     memory back to the host.
+ *   - Validation happens on the host before anything is enqueued. On any error
+ *     nothing is enqueued and the cache state is unchanged; sfkv_last_error()
+ *     returns a message for the calling thread.
+ *   - Handles are not thread-safe; calls on one handle must be serialised.
+ *
+ * Tensor layouts (row-major, contiguous, 16-byte aligned):
+ *   Q, K, V inputs : [n_tokens][num_heads][head_dim], bf16 or fp32
+ *   attend output  : [n_q][num_heads][head_dim], fp32
+ *   cache storage  : K codes [num_heads][capacity][head_dim] u8 (OCP E4M3FN),
+ *                    V codes likewise, positions [capacity] int32,
+ *                    scales [4][num_heads] fp32 (scale_k, inv_k, scale_v, inv_v);
+ *                    byte offsets from sfkv_cache_layout().
+ *
+ * Numerics (readings of what the pages leave open):
+ *   RoPE: interleaved pairs (x[2i], x[2i+1]), theta_i = base^(-2i/d), angles
+ *   in fp64 and cos/sin from the C library rounded once to fp32; keys rotated
+ *   in fp32 without fused multiply-add. Quantisation: y = fl(x * inv_scale),
+ *   clamp to +-448, round to nearest even E4M3FN. These make the stored bytes
+ *   reproducible bit for bit by any IEEE implementation of the same formulas.
+ */
+#ifndef SFKV_H
+#define SFKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sfkv_rope sfkv_rope;    /* host handle; table in caller device memory */
+typedef struct sfkv_cache sfkv_cache;  /* host handle; ring in caller device memory  */
+
+typedef enum {
+  SFKV_OK = 0,
+  SFKV_EINVAL = -1, /* bad argument: pointer, alignment, size, shape, dtype */
+  SFKV_ESTATE = -2, /* call out of order (write before calibrate, attend before write) */
+  SFKV_ERANGE = -3, /* positions would leave [0, max_position) or a rebase would go negative */
+  SFKV_EHIP = -4    /* a HIP runtime call or kernel launch failed */
+} sfkv_status;
+
+typedef enum { SFKV_BF16 = 0, SFKV_FP32 = 1 } sfkv_dtype;
+
+typedef struct {
+  int32_t num_heads;      /* >= 1 */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t capacity;       /* ring slots, >= 1 */
+  int32_t max_new_tokens; /* largest n_tokens of one write, in [1, capacity] */
+  /* num_heads * capacity * head_dim must be below 2^31 (one code plane < 2 GiB) */
+} sfkv_cache_cfg;
+
+/* ---- RoPE table ---------------------------------------------------------
+ * Rotation table shared by every cache of one head_dim: fp32 (cos, sin) pairs
+ * for positions 0 .. max_position (inclusive), [max_position + 1][head_dim/2].
+ * Built on the host once and uploaded; sfkv_rope_init synchronises `stream`
+ * before returning (set-up only, never in the per-step path).
+ * Source: "Do It Once, at Write Time" (RoPE applied once at write). */
+size_t sfkv_rope_bytes(int32_t head_dim, int32_t max_position);
+sfkv_status sfkv_rope_init(double base, int32_t head_dim, int32_t max_position,
+                           void *dev_mem, size_t bytes, void *stream, sfkv_rope **out);
+void sfkv_rope_destroy(sfkv_rope *rope);
+
+/* ---- Cache -----------------------------------------------------------------
+ * sfkv_cache_bytes: device bytes one cache needs. sfkv_cache_init carves the
+ * caller's buffer (256-byte aligned, at least that size), enqueues a clear of
+ * it on `stream` and returns an empty ring: no tokens, next position 0, no
+ * scales. The rope table must outlive the cache.
+ * Source: "Where the Time Went" (one cache per call) and "Do It Once, at Write
+ * Time" (ring storage). */
+size_t sfkv_cache_bytes(const sfkv_cache_cfg *cfg);
+sfkv_status sfkv_cache_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, void *dev_mem,
+                            size_t bytes, void *stream, sfkv_cache **out);
+void sfkv_cache_destroy(sfkv_cache *cache);
+
+/* sfkv_calibrate_scales: per-head scales from one frame k, v [n_tokens][H][d],
+ * computed on the device and kept there (no host readback): absmax over the
+ * frame of the keys rotated at the positions the next write will use, and of
+ * the raw values; scale = absmax/448 and inv = 448/absmax, divided in fp64 and
+ * rounded once to fp32 (1 and 1 for an all-zero head). Does not advance the
+ * ring. May be called again to re-calibrate.
+ * Errors: EINVAL (pointers, dtype, n_tokens outside [1, max_new_tokens]),
+ *         ERANGE (the frame's positions would reach max_position).
+ * Source: "Do It Once, at Write Time" (per-head scales calibrated once per
+ * session); "What Broke in Production" (scales stay on the device). */
+sfkv_status sfkv_calibrate_scales(sfkv_cache *cache, const void *k, const void *v,
+                                  sfkv_dtype dtype, int32_t n_tokens, void *stream);
+
+/* sfkv_cache_write: append one frame. Token i (0-based) goes to slot
+ * (write_slot + i) mod capacity at position next_pos + i; its key is rotated
+ * at that position and both key and value are quantised with the head's
+ * scale; positions[slot] is set. Then tokens += n, next_pos += n.
+ * Errors: EINVAL (pointers, dtype, n_tokens outside [1, max_new_tokens]),
+ *         ESTATE (no calibration yet),
+ *         ERANGE (next_pos + n_tokens > max_position of the rope table).
+ * Source: "Do It Once, at Write Time". */
+sfkv_status sfkv_cache_write(sfkv_cache *cache, const void *k, const void *v,
+                             sfkv_dtype dtype, int32_t n_tokens, void *stream);
+
+/* sfkv_attend: out = softmax(q k^T / sqrt(d)) v over every valid slot, per
+ * head, with no mask. q [n_q][H][d] are the queries of the most recent write
+ * (n_q must equal that write's n_tokens); they are rotated at that write's
+ * positions inside the kernel. Keys and values are the decoded FP8 codes times
+ * the head's scale. Slot order does not matter because every key carries its
+ * own rotation. Output is fp32 [n_q][H][d].
+ * `workspace` is device memory of at least sfkv_attend_workspace_bytes(cache,
+ * n_q) bytes (may be NULL when that is 0); calls on one stream may share it.
+ * Errors: EINVAL (pointers, dtype, n_q mismatch, workspace too small),
+ *         ESTATE (no write yet).
+ * Source: "Where the Time Went" (the call's attention over its whole cache);
+ * "Blackwell and Beyond Four GPUs" (FP8 attention taking per-head scales);
+ * "Do It Once, at Write Time" (time-order positions once the ring wraps). */
+size_t sfkv_attend_workspace_bytes(const sfkv_cache *cache, int32_t n_q);
+sfkv_status sfkv_attend(sfkv_cache *cache, const void *q, sfkv_dtype dtype, int32_t n_q,
+                        float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* sfkv_rebase_positions: subtract delta from every position with one delta
+ * rotation of the cached keys: each valid key's FP8 codes are rotated by
+ * -delta*theta in the code domain (the per-head scale cancels), clamped and
+ * re-encoded; values are untouched; positions[slot] -= delta for valid slots;
+ * next_pos -= delta; the last write's query positions move by -delta too, so
+ * attention is unchanged up to rounding. Resetting positions to 0 is
+ * delta = next_pos.
+ * Errors: ERANGE (delta < 0 or delta > next_pos).
+ * Source: "Do It Once, at Write Time" (positions reset every 42 steps; a single
+ * delta rotation of the cached window at each reset). */
+sfkv_status sfkv_rebase_positions(sfkv_cache *cache, int64_t delta, void *stream);
+
+/* Host mirror of the ring state (no device access). Any out pointer may be NULL.
+ * tokens: written this session; next_pos: position of the next token;
+ * write_slot: tokens mod capacity; n_valid: min(tokens, capacity). */
+sfkv_status sfkv_cache_state(const sfkv_cache *cache, int64_t *tokens, int64_t *next_pos,
+                             int32_t *write_slot, int32_t *n_valid);
+
+/* Byte offsets of the K codes, V codes, positions and scales inside the
+ * cache's device buffer (for inspection by tests and tools). */
+sfkv_status sfkv_cache_layout(const sfkv_cache *cache, size_t *k_off, size_t *v_off,
+                              size_t *pos_off, size_t *scale_off);
+
+const char *sfkv_status_string(sfkv_status status);
+const char *sfkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SFKV_H */

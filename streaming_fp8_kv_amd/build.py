@@ -1,0 +1,62 @@
+"""Build libsfkv.so for gfx950 in-tree with hipcc.
+
+Usage: ``python -m streaming_fp8_kv_amd.build`` (or ``build()`` from Python).
+Always recompiles every source.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OBJ = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libsfkv.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = os.environ.get("SFKV_ARCH", "gfx950")
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    # packed fp32 VALU ops stay disabled; the compiler must not form them
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+# (source, extra flags). The write-side kernels decide stored bytes with fp32
+# arithmetic, so no multiply-add contraction there; the host library builds the
+# RoPE table with libm and must not use fast-math either.
+SOURCES = [
+    ("cache_kernels.hip", ["-ffp-contract=off"]),
+    ("attend_kernel.hip", []),
+    ("sfkv_api.cpp", ["-x", "hip", "-ffp-contract=off", "-fno-fast-math"]),
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
+            if "packed-fp32-ops" not in ln and "argument unused during compilation" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+    return msgs
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    objs = []
+    for src, extra in SOURCES:
+        obj = os.path.join(OBJ, src.rsplit(".", 1)[0] + ".o")
+        msgs = _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and msgs:
+            print("\n".join(msgs))
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,227 @@
+// Write-side kernels of the FP8 ring cache for gfx950: per-head scale
+// calibration, the fused RoPE + scale + E4M3 + ring-scatter write, and the
+// code-domain delta rotation applied at a position reset.
+//
+// Method: Runway Characters post, "Do It Once, at Write Time" -- rotate and
+// quantise each frame once as it enters the ring, with per-head scales
+// calibrated once per session, and apply one delta rotation to the cached
+// window when positions reset.
+//
+// Every float operation that decides a stored byte is an IEEE fp32 operation
+// in a fixed order with no fused multiply-add (this file is compiled with
+// -ffp-contract=off and the rotations also carry the pragma), so the bytes are
+// reproducible by any other IEEE implementation of the same formulas.
+#include "sfkv_internal.h"
+
+namespace sfkv {
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Load 8 consecutive input elements (bf16 or fp32) as fp32.
+__device__ inline void load8(const void *base, size_t elem, int dtype, float x[8]) {
+  if (dtype == 0) {
+    uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem);
+    float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
+// Forward rotation of one interleaved pair: a' = a*c - b*s, b' = a*s + b*c,
+// each product and sum rounded to fp32 separately.
+__device__ inline void rotate_pair(float &a, float &b, RopePair cs) {
+#pragma clang fp contract(off)
+  float ac = a * cs.c, bs = b * cs.s, as = a * cs.s, bc = b * cs.c;
+  a = ac - bs;
+  b = as + bc;
+}
+
+// Rotation by the negative angle: a' = a*c + b*s, b' = b*c - a*s.
+__device__ inline void rotate_pair_back(float &a, float &b, RopePair cs) {
+#pragma clang fp contract(off)
+  float ac = a * cs.c, bs = b * cs.s, bc = b * cs.c, as = a * cs.s;
+  a = ac + bs;
+  b = bc - as;
+}
+
+// Clamp to the E4M3 range, then round to nearest even (hardware convert on
+// gfx950 produces OCP E4M3FN codes). Four values -> one little-endian word.
+__device__ inline uint32_t encode4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+  c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+  d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+__device__ inline void decode4(uint32_t w, float *x) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+}
+
+__device__ inline float scaled(float x, float inv) {
+#pragma clang fp contract(off)
+  return x * inv;
+}
+
+// One thread = 8 consecutive dims of one (token, head): 16 B of bf16 K and V
+// in, 8 B of K codes and 8 B of V codes out. Consecutive threads walk the dims
+// of a head, then the heads of a token, so the reads are fully coalesced and
+// every 128-byte row of a code plane is written by 16 adjacent lanes.
+__global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
+  // 32-bit indexing: the host keeps every code plane below 2^31 bytes.
+  const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 3;
+  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const unsigned total = static_cast<unsigned>(a.n) * a.heads * chunks;
+  if (idx >= total) return;
+  const int c = static_cast<int>(idx % chunks);
+  const unsigned th = idx / chunks;
+  const int h = static_cast<int>(th % static_cast<unsigned>(a.heads));
+  const int i = static_cast<int>(th / static_cast<unsigned>(a.heads));
+
+  int slot = a.slot0 + i;
+  if (slot >= a.capacity) slot -= a.capacity;   // n <= capacity, so one wrap at most
+  const int p = a.pos0 + i;
+  const size_t in_elem = (static_cast<size_t>(i) * a.heads + h) * a.head_dim + c * 8;
+  const size_t out_off = (static_cast<size_t>(h) * a.capacity + slot) * a.head_dim + c * 8;
+
+  const float inv_k = a.scales[a.heads + h];
+  const float inv_v = a.scales[3 * a.heads + h];
+
+  float x[8];
+  load8(a.k, in_elem, a.dtype, x);
+  const RopePair *row = a.rope + static_cast<size_t>(p) * (a.head_dim >> 1) + c * 4;
+  const float4 cs01 = *reinterpret_cast<const float4 *>(row);
+  const float4 cs23 = *reinterpret_cast<const float4 *>(row + 2);
+  rotate_pair(x[0], x[1], RopePair{cs01.x, cs01.y});
+  rotate_pair(x[2], x[3], RopePair{cs01.z, cs01.w});
+  rotate_pair(x[4], x[5], RopePair{cs23.x, cs23.y});
+  rotate_pair(x[6], x[7], RopePair{cs23.z, cs23.w});
+  uint2 kw;
+  kw.x = encode4(scaled(x[0], inv_k), scaled(x[1], inv_k), scaled(x[2], inv_k), scaled(x[3], inv_k));
+  kw.y = encode4(scaled(x[4], inv_k), scaled(x[5], inv_k), scaled(x[6], inv_k), scaled(x[7], inv_k));
+  *reinterpret_cast<uint2 *>(a.k8 + out_off) = kw;
+
+  load8(a.v, in_elem, a.dtype, x);
+  uint2 vw;
+  vw.x = encode4(scaled(x[0], inv_v), scaled(x[1], inv_v), scaled(x[2], inv_v), scaled(x[3], inv_v));
+  vw.y = encode4(scaled(x[4], inv_v), scaled(x[5], inv_v), scaled(x[6], inv_v), scaled(x[7], inv_v));
+  *reinterpret_cast<uint2 *>(a.v8 + out_off) = vw;
+
+  if (h == 0 && c == 0) a.pos[slot] = p;
+}
+
+__device__ inline float wave_max(float m) {
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  return m;
+}
+
+// One block per (head, tensor): absmax of the rotated keys (blockIdx.y == 0)
+// or of the raw values (blockIdx.y == 1) over the frame, then the two scales.
+// The maximum is exact and order-free, so the result is deterministic.
+__global__ __launch_bounds__(256) void calibrate_kernel(CalibrateLaunch a) {
+  const int h = blockIdx.x;
+  const bool keys = blockIdx.y == 0;
+  const int pairs = a.head_dim >> 1;
+  const void *src = keys ? a.k : a.v;
+  float m = 0.0f;
+  const int total = a.n * pairs;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int i = e / pairs, pr = e - i * pairs;
+    const size_t elem = (static_cast<size_t>(i) * a.heads + h) * a.head_dim + 2 * pr;
+    float x0, x1;
+    if (a.dtype == 0) {
+      uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(src) + elem);
+      x0 = bf16_lo(w); x1 = bf16_hi(w);
+    } else {
+      float2 w = *reinterpret_cast<const float2 *>(static_cast<const float *>(src) + elem);
+      x0 = w.x; x1 = w.y;
+    }
+    if (keys) rotate_pair(x0, x1, a.rope[static_cast<size_t>(a.pos0 + i) * pairs + pr]);
+    m = fmaxf(m, fmaxf(fabsf(x0), fabsf(x1)));
+  }
+  m = wave_max(m);
+  __shared__ float partial[4];
+  if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (blockDim.x >> 6); ++w) m = fmaxf(m, partial[w]);
+    m = fmaxf(m, partial[0]);
+    float scale = 1.0f, inv = 1.0f;
+    if (m > 0.0f) {
+      scale = static_cast<float>(static_cast<double>(m) / 448.0);
+      inv = static_cast<float>(448.0 / static_cast<double>(m));
+    }
+    const int base = keys ? 0 : 2 * a.heads;
+    a.scales[base + h] = scale;
+    a.scales[base + a.heads + h] = inv;
+  }
+}
+
+// One thread = 16 code bytes (8 pairs) of one valid (head, slot) row: decode
+// exactly to fp32, rotate by -delta, clamp, re-encode, store in place. The
+// per-head scale cancels because the rotation is linear.
+__global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunch a) {
+  const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 4;
+  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const unsigned total = static_cast<unsigned>(a.heads) * a.n_valid * chunks;
+  if (idx >= total) return;
+  const int c = static_cast<int>(idx % chunks);
+  const unsigned row = idx / chunks;
+  const int slot = static_cast<int>(row % static_cast<unsigned>(a.n_valid));
+  const int h = static_cast<int>(row / static_cast<unsigned>(a.n_valid));
+  uint8_t *ptr = a.k8 + (static_cast<size_t>(h) * a.capacity + slot) * a.head_dim + c * 16;
+  uint4 w = *reinterpret_cast<const uint4 *>(ptr);
+  float x[16];
+  decode4(w.x, x);
+  decode4(w.y, x + 4);
+  decode4(w.z, x + 8);
+  decode4(w.w, x + 12);
+  const RopePair *cs = a.rope_row + c * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rotate_pair_back(x[2 * j], x[2 * j + 1], cs[j]);
+  uint4 o;
+  o.x = encode4(x[0], x[1], x[2], x[3]);
+  o.y = encode4(x[4], x[5], x[6], x[7]);
+  o.z = encode4(x[8], x[9], x[10], x[11]);
+  o.w = encode4(x[12], x[13], x[14], x[15]);
+  *reinterpret_cast<uint4 *>(ptr) = o;
+  if (h == 0 && c == 0) a.pos[slot] -= a.delta;
+}
+
+inline unsigned blocks_for(size_t threads, unsigned per_block) {
+  return static_cast<unsigned>((threads + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+hipError_t launch_write(const WriteLaunch &a, hipStream_t s) {
+  const size_t threads = static_cast<size_t>(a.n) * a.heads * (a.head_dim >> 3);
+  hipLaunchKernelGGL(write_kernel, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s) {
+  hipLaunchKernelGGL(calibrate_kernel, dim3(a.heads, 2), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s) {
+  const size_t threads = static_cast<size_t>(a.heads) * a.n_valid * (a.head_dim >> 4);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(rebase_kernel, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sfkv

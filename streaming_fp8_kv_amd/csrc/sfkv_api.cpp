@@ -1,0 +1,350 @@
+// Host side of the C ABI declared in sfkv.h: argument validation, the
+// host-mirrored ring state, the RoPE table, and kernel launches.
+//
+// The ring scalars (tokens written, next position, last write) are a pure
+// function of the call sequence, so they live here and reach the kernels by
+// value: no call reads device memory back, and a captured stream replays the
+// exact launches it recorded (Runway Characters post, "What Broke in
+// Production": a single per-step device-to-host read was the worst regression).
+#include "sfkv.h"
+#include "sfkv_internal.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+struct sfkv_rope {
+  double base;
+  int32_t head_dim;
+  int32_t max_position;
+  sfkv::RopePair *table;  // device: [max_position + 1][head_dim / 2]
+};
+
+struct sfkv_cache {
+  sfkv_cache_cfg cfg;
+  const sfkv_rope *rope;
+  uint8_t *base;
+  size_t k_off, v_off, pos_off, scale_off, bytes;
+  int64_t tokens;
+  int64_t next_pos;
+  int64_t last_pos0;
+  int32_t last_n;
+  bool calibrated;
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+sfkv_status fail(sfkv_status s, const std::string &msg) {
+  g_error = msg;
+  return s;
+}
+
+sfkv_status ok() {
+  g_error.clear();
+  return SFKV_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+bool valid_head_dim(int32_t d) { return d == 64 || d == 128; }
+
+struct Layout {
+  size_t k, v, pos, scale, total;
+};
+
+Layout layout_of(const sfkv_cache_cfg &c) {
+  Layout l;
+  const size_t plane = static_cast<size_t>(c.num_heads) * c.capacity * c.head_dim;
+  l.k = 0;
+  l.v = align_up(l.k + plane, 256);
+  l.pos = align_up(l.v + plane, 256);
+  l.scale = align_up(l.pos + static_cast<size_t>(c.capacity) * sizeof(int32_t), 256);
+  l.total = align_up(l.scale + 4 * static_cast<size_t>(c.num_heads) * sizeof(float), 256);
+  return l;
+}
+
+sfkv_status check_cfg(const sfkv_cache_cfg *c) {
+  if (!c) return fail(SFKV_EINVAL, "cfg is NULL");
+  if (c->num_heads < 1 || c->num_heads > 4096) return fail(SFKV_EINVAL, "num_heads must be in [1, 4096]");
+  if (!valid_head_dim(c->head_dim)) return fail(SFKV_EINVAL, "head_dim must be 64 or 128");
+  if (c->capacity < 1 || c->capacity > (1 << 24)) return fail(SFKV_EINVAL, "capacity must be in [1, 2^24]");
+  if (c->max_new_tokens < 1 || c->max_new_tokens > c->capacity)
+    return fail(SFKV_EINVAL, "max_new_tokens must be in [1, capacity]");
+  if (static_cast<size_t>(c->num_heads) * c->capacity * c->head_dim >= (size_t{1} << 31))
+    return fail(SFKV_EINVAL, "num_heads * capacity * head_dim must be below 2^31");
+  return SFKV_OK;
+}
+
+sfkv_status check_frame(const sfkv_cache *c, const void *k, const void *v, sfkv_dtype dtype,
+                        int32_t n) {
+  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (!k || !v) return fail(SFKV_EINVAL, "k and v must be device pointers");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(SFKV_EINVAL, "k and v must be 16-byte aligned");
+  if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
+  if (n < 1 || n > c->cfg.max_new_tokens) return fail(SFKV_EINVAL, "n_tokens must be in [1, max_new_tokens]");
+  if (c->next_pos + n > c->rope->max_position)
+    return fail(SFKV_ERANGE, "positions of this frame would reach max_position");
+  return SFKV_OK;
+}
+
+sfkv_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(SFKV_EHIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sfkv_status_string(sfkv_status s) {
+  switch (s) {
+    case SFKV_OK: return "ok";
+    case SFKV_EINVAL: return "invalid argument";
+    case SFKV_ESTATE: return "call out of order";
+    case SFKV_ERANGE: return "position out of range";
+    case SFKV_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *sfkv_last_error(void) { return g_error.c_str(); }
+
+size_t sfkv_rope_bytes(int32_t head_dim, int32_t max_position) {
+  if (!valid_head_dim(head_dim) || max_position < 1) return 0;
+  return (static_cast<size_t>(max_position) + 1) * (head_dim / 2) * sizeof(sfkv::RopePair);
+}
+
+sfkv_status sfkv_rope_init(double base, int32_t head_dim, int32_t max_position, void *dev_mem,
+                           size_t bytes, void *stream, sfkv_rope **out) {
+  if (!out) return fail(SFKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!valid_head_dim(head_dim)) return fail(SFKV_EINVAL, "head_dim must be 64 or 128");
+  if (max_position < 1 || max_position > (1 << 26)) return fail(SFKV_EINVAL, "max_position must be in [1, 2^26]");
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(SFKV_EINVAL, "base must be finite and > 1");
+  const size_t need = sfkv_rope_bytes(head_dim, max_position);
+  if (!dev_mem || !aligned(dev_mem, 256)) return fail(SFKV_EINVAL, "dev_mem must be 256-byte aligned device memory");
+  if (bytes < need) return fail(SFKV_EINVAL, "dev_mem smaller than sfkv_rope_bytes()");
+
+  // theta_i = base^((-2 i) / d); angle = p * theta_i in fp64; cos and sin from
+  // the C library, each rounded once to fp32.
+  const int half = head_dim / 2;
+  std::vector<double> theta(half);
+  for (int i = 0; i < half; ++i) theta[i] = std::pow(base, (-2.0 * static_cast<double>(i)) / static_cast<double>(head_dim));
+  std::vector<sfkv::RopePair> host(static_cast<size_t>(max_position + 1) * half);
+  for (int64_t p = 0; p <= max_position; ++p) {
+    for (int i = 0; i < half; ++i) {
+      const double ang = static_cast<double>(p) * theta[i];
+      host[static_cast<size_t>(p) * half + i] = sfkv::RopePair{static_cast<float>(std::cos(ang)),
+                                                               static_cast<float>(std::sin(ang))};
+    }
+  }
+  hipError_t e = hipMemcpyAsync(dev_mem, host.data(), need, hipMemcpyHostToDevice, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return fail(SFKV_EHIP, std::string("rope upload failed: ") + hipGetErrorString(e));
+  sfkv_rope *r = new (std::nothrow) sfkv_rope;
+  if (!r) return fail(SFKV_EINVAL, "out of host memory");
+  r->base = base;
+  r->head_dim = head_dim;
+  r->max_position = max_position;
+  r->table = static_cast<sfkv::RopePair *>(dev_mem);
+  *out = r;
+  return ok();
+}
+
+void sfkv_rope_destroy(sfkv_rope *rope) { delete rope; }
+
+size_t sfkv_cache_bytes(const sfkv_cache_cfg *cfg) {
+  if (check_cfg(cfg) != SFKV_OK) return 0;
+  return layout_of(*cfg).total;
+}
+
+sfkv_status sfkv_cache_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, void *dev_mem,
+                            size_t bytes, void *stream, sfkv_cache **out) {
+  if (!out) return fail(SFKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  sfkv_status st = check_cfg(cfg);
+  if (st != SFKV_OK) return st;
+  if (!rope) return fail(SFKV_EINVAL, "rope is NULL");
+  if (rope->head_dim != cfg->head_dim) return fail(SFKV_EINVAL, "rope head_dim differs from cfg head_dim");
+  const Layout l = layout_of(*cfg);
+  if (!dev_mem || !aligned(dev_mem, 256)) return fail(SFKV_EINVAL, "dev_mem must be 256-byte aligned device memory");
+  if (bytes < l.total) return fail(SFKV_EINVAL, "dev_mem smaller than sfkv_cache_bytes()");
+  hipError_t e = hipMemsetAsync(dev_mem, 0, l.total, as_stream(stream));
+  if (e != hipSuccess) return fail(SFKV_EHIP, std::string("cache clear failed: ") + hipGetErrorString(e));
+  sfkv_cache *c = new (std::nothrow) sfkv_cache;
+  if (!c) return fail(SFKV_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->rope = rope;
+  c->base = static_cast<uint8_t *>(dev_mem);
+  c->k_off = l.k;
+  c->v_off = l.v;
+  c->pos_off = l.pos;
+  c->scale_off = l.scale;
+  c->bytes = l.total;
+  c->tokens = 0;
+  c->next_pos = 0;
+  c->last_pos0 = 0;
+  c->last_n = 0;
+  c->calibrated = false;
+  *out = c;
+  return ok();
+}
+
+void sfkv_cache_destroy(sfkv_cache *cache) { delete cache; }
+
+sfkv_status sfkv_calibrate_scales(sfkv_cache *c, const void *k, const void *v, sfkv_dtype dtype,
+                                  int32_t n, void *stream) {
+  sfkv_status st = check_frame(c, k, v, dtype, n);
+  if (st != SFKV_OK) return st;
+  sfkv::CalibrateLaunch a;
+  a.k = k;
+  a.v = v;
+  a.dtype = dtype;
+  a.n = n;
+  a.heads = c->cfg.num_heads;
+  a.head_dim = c->cfg.head_dim;
+  a.pos0 = static_cast<int>(c->next_pos);
+  a.rope = c->rope->table;
+  a.scales = reinterpret_cast<float *>(c->base + c->scale_off);
+  st = launched(sfkv::launch_calibrate(a, as_stream(stream)));
+  if (st == SFKV_OK) c->calibrated = true;
+  return st;
+}
+
+sfkv_status sfkv_cache_write(sfkv_cache *c, const void *k, const void *v, sfkv_dtype dtype,
+                             int32_t n, void *stream) {
+  sfkv_status st = check_frame(c, k, v, dtype, n);
+  if (st != SFKV_OK) return st;
+  if (!c->calibrated) return fail(SFKV_ESTATE, "cache_write before calibrate_scales");
+  sfkv::WriteLaunch a;
+  a.k = k;
+  a.v = v;
+  a.dtype = dtype;
+  a.n = n;
+  a.heads = c->cfg.num_heads;
+  a.head_dim = c->cfg.head_dim;
+  a.capacity = c->cfg.capacity;
+  a.slot0 = static_cast<int>(c->tokens % c->cfg.capacity);
+  a.pos0 = static_cast<int>(c->next_pos);
+  a.rope = c->rope->table;
+  a.k8 = c->base + c->k_off;
+  a.v8 = c->base + c->v_off;
+  a.pos = reinterpret_cast<int32_t *>(c->base + c->pos_off);
+  a.scales = reinterpret_cast<const float *>(c->base + c->scale_off);
+  st = launched(sfkv::launch_write(a, as_stream(stream)));
+  if (st != SFKV_OK) return st;
+  c->last_pos0 = c->next_pos;
+  c->last_n = n;
+  c->tokens += n;
+  c->next_pos += n;
+  return SFKV_OK;
+}
+
+static int n_valid_of(const sfkv_cache *c) {
+  return static_cast<int>(c->tokens < c->cfg.capacity ? c->tokens : c->cfg.capacity);
+}
+
+static size_t attend_ws_bytes(const sfkv_cache_cfg &cfg, int splits, int32_t n_q) {
+  if (splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(splits) * n_q * cfg.num_heads;
+  return align_up(rows * cfg.head_dim * sizeof(float), 256) + align_up(rows * 2 * sizeof(float), 256);
+}
+
+size_t sfkv_attend_workspace_bytes(const sfkv_cache *c, int32_t n_q) {
+  if (!c || n_q < 1 || n_q > c->cfg.max_new_tokens) return 0;
+  const int s = sfkv::attend_splits(n_q, c->cfg.num_heads, c->cfg.capacity);
+  return attend_ws_bytes(c->cfg, s, n_q);
+}
+
+sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t n_q, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (c->last_n == 0) return fail(SFKV_ESTATE, "attend before any cache_write");
+  if (!q || !out) return fail(SFKV_EINVAL, "q and out must be device pointers");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(SFKV_EINVAL, "q and out must be 16-byte aligned");
+  if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
+  if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
+  const int nv = n_valid_of(c);
+  const int splits = sfkv::attend_splits(n_q, c->cfg.num_heads, nv);
+  const size_t need = attend_ws_bytes(c->cfg, splits, n_q);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return fail(SFKV_EINVAL, "workspace missing, smaller than sfkv_attend_workspace_bytes() or not 256-byte aligned");
+  sfkv::AttendLaunch a;
+  a.q = q;
+  a.dtype = dtype;
+  a.n_q = n_q;
+  a.heads = c->cfg.num_heads;
+  a.head_dim = c->cfg.head_dim;
+  a.capacity = c->cfg.capacity;
+  a.n_valid = nv;
+  a.qpos0 = static_cast<int>(c->last_pos0);
+  a.rope = c->rope->table;
+  a.k8 = c->base + c->k_off;
+  a.v8 = c->base + c->v_off;
+  a.scales = reinterpret_cast<const float *>(c->base + c->scale_off);
+  a.out = out;
+  a.splits = splits;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (splits > 1) {
+    const size_t rows = static_cast<size_t>(splits) * n_q * c->cfg.num_heads;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                          align_up(rows * c->cfg.head_dim * sizeof(float), 256));
+  }
+  return launched(sfkv::launch_attend(a, as_stream(stream)));
+}
+
+sfkv_status sfkv_rebase_positions(sfkv_cache *c, int64_t delta, void *stream) {
+  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (delta < 0 || delta > c->next_pos) return fail(SFKV_ERANGE, "delta must be in [0, next_pos]");
+  if (delta > 0) {
+    const int nv = n_valid_of(c);
+    if (nv > 0) {
+      sfkv::RebaseLaunch a;
+      a.k8 = c->base + c->k_off;
+      a.pos = reinterpret_cast<int32_t *>(c->base + c->pos_off);
+      a.heads = c->cfg.num_heads;
+      a.head_dim = c->cfg.head_dim;
+      a.capacity = c->cfg.capacity;
+      a.n_valid = nv;
+      a.delta = static_cast<int>(delta);
+      a.rope_row = c->rope->table + static_cast<size_t>(delta) * (c->cfg.head_dim / 2);
+      sfkv_status st = launched(sfkv::launch_rebase(a, as_stream(stream)));
+      if (st != SFKV_OK) return st;
+    }
+  }
+  c->next_pos -= delta;
+  c->last_pos0 -= delta;
+  return ok();
+}
+
+sfkv_status sfkv_cache_state(const sfkv_cache *c, int64_t *tokens, int64_t *next_pos,
+                             int32_t *write_slot, int32_t *n_valid) {
+  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (tokens) *tokens = c->tokens;
+  if (next_pos) *next_pos = c->next_pos;
+  if (write_slot) *write_slot = static_cast<int32_t>(c->tokens % c->cfg.capacity);
+  if (n_valid) *n_valid = n_valid_of(c);
+  return ok();
+}
+
+sfkv_status sfkv_cache_layout(const sfkv_cache *c, size_t *k_off, size_t *v_off, size_t *pos_off,
+                              size_t *scale_off) {
+  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (k_off) *k_off = c->k_off;
+  if (v_off) *v_off = c->v_off;
+  if (pos_off) *pos_off = c->pos_off;
+  if (scale_off) *scale_off = c->scale_off;
+  return ok();
+}
+
+}  // extern "C"

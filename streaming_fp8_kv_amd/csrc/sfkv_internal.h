@@ -1,0 +1,64 @@
+// Internal declarations shared by the host library and the kernel sources.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace sfkv {
+
+// RoPE table row: (cos, sin) of one pair at one position.
+struct RopePair {
+  float c, s;
+};
+
+struct WriteLaunch {
+  const void *k, *v;
+  int dtype;        // 0 bf16, 1 fp32
+  int n, heads, head_dim, capacity;
+  int slot0;        // ring slot of token 0
+  int pos0;         // position of token 0
+  const RopePair *rope;
+  uint8_t *k8, *v8;
+  int32_t *pos;
+  const float *scales;  // [4][heads]
+};
+
+struct CalibrateLaunch {
+  const void *k, *v;
+  int dtype, n, heads, head_dim, pos0;
+  const RopePair *rope;
+  float *scales;
+};
+
+struct RebaseLaunch {
+  uint8_t *k8;
+  int32_t *pos;
+  int heads, head_dim, capacity, n_valid;
+  int delta;
+  const RopePair *rope_row;  // table row at position delta
+};
+
+struct AttendLaunch {
+  const void *q;
+  int dtype, n_q, heads, head_dim, capacity, n_valid;
+  int qpos0;                 // position of query row 0
+  const RopePair *rope;
+  const uint8_t *k8, *v8;
+  const float *scales;
+  float *out;
+  int splits;                // key-range splits; 1 writes `out` directly
+  float *part_o;             // [splits][n_q][heads][head_dim] when splits > 1
+  float *part_ml;            // [splits][n_q][heads][2]
+};
+
+hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s);
+hipError_t launch_write(const WriteLaunch &a, hipStream_t s);
+hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s);
+hipError_t launch_attend(const AttendLaunch &a, hipStream_t s);
+
+// Attention tiling shared by the launcher and the workspace sizing.
+constexpr int kAttendQueriesPerBlock = 64;
+constexpr int kAttendKeysPerTile = 64;
+int attend_splits(int n_q, int heads, int capacity);
+
+}  // namespace sfkv

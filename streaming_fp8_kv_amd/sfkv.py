@@ -1,0 +1,251 @@
+"""ctypes binding of libsfkv.so (the C ABI in include/sfkv.h).
+
+Argument marshalling only: every step of the cache path runs in the HIP
+kernels behind the C ABI. PyTorch provides device memory and the current HIP
+stream. The module raises on import when the library has not been built; there
+is no fallback implementation.
+
+The function names mirror the C entry points without their ``sfkv_`` prefix:
+``rope_bytes``, ``rope_init``, ``cache_bytes``, ``cache_init``,
+``calibrate_scales``, ``cache_write``, ``attend_workspace_bytes``, ``attend``,
+``rebase_positions``, ``cache_state``, ``cache_layout``. ``Rope`` and
+``RingCache`` bundle a handle with the torch buffer it lives in.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsfkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with `python -m streaming_fp8_kv_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, EINVAL, ESTATE, ERANGE, EHIP = 0, -1, -2, -3, -4
+BF16, FP32 = 0, 1
+
+# every symbol include/sfkv.h declares
+SYMBOLS = (
+    "sfkv_rope_bytes", "sfkv_rope_init", "sfkv_rope_destroy",
+    "sfkv_cache_bytes", "sfkv_cache_init", "sfkv_cache_destroy",
+    "sfkv_calibrate_scales", "sfkv_cache_write",
+    "sfkv_attend_workspace_bytes", "sfkv_attend", "sfkv_rebase_positions",
+    "sfkv_cache_state", "sfkv_cache_layout", "sfkv_status_string", "sfkv_last_error",
+)
+
+
+class CacheConfig(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("max_new_tokens", ctypes.c_int32)]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_P = ctypes.POINTER
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("sfkv_rope_bytes", _sz, _i32, _i32)
+_sig("sfkv_rope_init", ctypes.c_int, ctypes.c_double, _i32, _i32, _vp, _sz, _vp, _P(_vp))
+_sig("sfkv_rope_destroy", None, _vp)
+_sig("sfkv_cache_bytes", _sz, _P(CacheConfig))
+_sig("sfkv_cache_init", ctypes.c_int, _P(CacheConfig), _vp, _vp, _sz, _vp, _P(_vp))
+_sig("sfkv_cache_destroy", None, _vp)
+_sig("sfkv_calibrate_scales", ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i32, _vp)
+_sig("sfkv_cache_write", ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i32, _vp)
+_sig("sfkv_attend_workspace_bytes", _sz, _vp, _i32)
+_sig("sfkv_attend", ctypes.c_int, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
+_sig("sfkv_rebase_positions", ctypes.c_int, _vp, _i64, _vp)
+_sig("sfkv_cache_state", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i32), _P(_i32))
+_sig("sfkv_cache_layout", ctypes.c_int, _vp, _P(_sz), _P(_sz), _P(_sz), _P(_sz))
+_sig("sfkv_status_string", ctypes.c_char_p, ctypes.c_int)
+_sig("sfkv_last_error", ctypes.c_char_p)
+
+
+class SfkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_lib.sfkv_status_string(status).decode()} ({status}): {message}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != OK:
+        raise SfkvError(status, _lib.sfkv_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError("inputs must be bfloat16 or float32")
+
+
+def _frame(t: torch.Tensor, heads: int, head_dim: int) -> torch.Tensor:
+    if not t.is_cuda or not t.is_contiguous() or t.dim() != 3 or tuple(t.shape[1:]) != (heads, head_dim):
+        raise ValueError("expected a contiguous CUDA tensor of shape [n, heads, head_dim]")
+    return t
+
+
+# ---- C entry points -----------------------------------------------------------
+def rope_bytes(head_dim: int, max_position: int) -> int:
+    return int(_lib.sfkv_rope_bytes(head_dim, max_position))
+
+
+def rope_init(base: float, head_dim: int, max_position: int, buf: torch.Tensor, stream=None) -> int:
+    h = _vp()
+    _check(_lib.sfkv_rope_init(base, head_dim, max_position, buf.data_ptr(), buf.numel(),
+                               _stream(stream), ctypes.byref(h)))
+    return h.value
+
+
+def cache_bytes(cfg: CacheConfig) -> int:
+    return int(_lib.sfkv_cache_bytes(ctypes.byref(cfg)))
+
+
+def cache_init(cfg: CacheConfig, rope_handle: int, buf: torch.Tensor, stream=None) -> int:
+    h = _vp()
+    _check(_lib.sfkv_cache_init(ctypes.byref(cfg), rope_handle, buf.data_ptr(), buf.numel(),
+                                _stream(stream), ctypes.byref(h)))
+    return h.value
+
+
+def calibrate_scales(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _check(_lib.sfkv_calibrate_scales(handle, k.data_ptr(), v.data_ptr(), _dtype_code(k),
+                                      k.shape[0], _stream(stream)))
+
+
+def cache_write(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _check(_lib.sfkv_cache_write(handle, k.data_ptr(), v.data_ptr(), _dtype_code(k),
+                                 k.shape[0], _stream(stream)))
+
+
+def attend_workspace_bytes(handle: int, n_q: int) -> int:
+    return int(_lib.sfkv_attend_workspace_bytes(handle, n_q))
+
+
+def attend(handle: int, q: torch.Tensor, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+           stream=None):
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.sfkv_attend(handle, q.data_ptr(), _dtype_code(q), q.shape[0], out.data_ptr(),
+                            ws_ptr, ws_len, _stream(stream)))
+
+
+def rebase_positions(handle: int, delta: int, stream=None):
+    _check(_lib.sfkv_rebase_positions(handle, int(delta), _stream(stream)))
+
+
+def cache_state(handle: int) -> dict:
+    t, p, s, n = _i64(), _i64(), _i32(), _i32()
+    _check(_lib.sfkv_cache_state(handle, ctypes.byref(t), ctypes.byref(p), ctypes.byref(s), ctypes.byref(n)))
+    return {"tokens": t.value, "next_pos": p.value, "write_slot": s.value, "n_valid": n.value}
+
+
+def cache_layout(handle: int) -> dict:
+    k, v, p, s = _sz(), _sz(), _sz(), _sz()
+    _check(_lib.sfkv_cache_layout(handle, ctypes.byref(k), ctypes.byref(v), ctypes.byref(p), ctypes.byref(s)))
+    return {"k": k.value, "v": v.value, "pos": p.value, "scales": s.value}
+
+
+# ---- owners -------------------------------------------------------------------
+class Rope:
+    """RoPE table in a torch device buffer, shared by every cache of one head_dim."""
+
+    def __init__(self, head_dim: int, max_position: int = 65536, base: float = 10000.0,
+                 device="cuda", stream=None):
+        self.head_dim, self.max_position, self.base = head_dim, max_position, base
+        n = rope_bytes(head_dim, max_position)
+        if n == 0:
+            raise ValueError("invalid head_dim or max_position")
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self.handle = rope_init(base, head_dim, max_position, self.buf, stream)
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            _lib.sfkv_rope_destroy(self.handle)
+            self.handle = None
+
+
+class RingCache:
+    """One ring cache: its device buffer, handle and views of its contents."""
+
+    def __init__(self, rope: Rope, heads: int, capacity: int, max_new_tokens: Optional[int] = None,
+                 device="cuda", stream=None):
+        self.rope = rope
+        self.cfg = CacheConfig(heads, rope.head_dim, capacity, max_new_tokens or capacity)
+        n = cache_bytes(self.cfg)
+        if n == 0:
+            raise ValueError("invalid cache configuration")
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self.handle = cache_init(self.cfg, rope.handle, self.buf, stream)
+        self.layout = cache_layout(self.handle)
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            _lib.sfkv_cache_destroy(self.handle)
+            self.handle = None
+
+    # compute calls
+    def calibrate_scales(self, k, v, stream=None):
+        calibrate_scales(self.handle, _frame(k, self.cfg.num_heads, self.cfg.head_dim),
+                         _frame(v, self.cfg.num_heads, self.cfg.head_dim), stream)
+
+    def cache_write(self, k, v, stream=None):
+        cache_write(self.handle, _frame(k, self.cfg.num_heads, self.cfg.head_dim),
+                    _frame(v, self.cfg.num_heads, self.cfg.head_dim), stream)
+
+    def workspace_bytes(self, n_q: int) -> int:
+        return attend_workspace_bytes(self.handle, n_q)
+
+    def attend(self, q, out=None, workspace=None, stream=None):
+        q = _frame(q, self.cfg.num_heads, self.cfg.head_dim)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            need = self.workspace_bytes(q.shape[0])
+            if need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        attend(self.handle, q, out, workspace, stream)
+        return out
+
+    def rebase_positions(self, delta: int, stream=None):
+        rebase_positions(self.handle, delta, stream)
+
+    def state(self) -> dict:
+        return cache_state(self.handle)
+
+    # views into the device buffer (no copies)
+    def k_codes(self) -> torch.Tensor:
+        c = self.cfg
+        n = c.num_heads * c.capacity * c.head_dim
+        return self.buf[self.layout["k"]:self.layout["k"] + n].view(c.num_heads, c.capacity, c.head_dim)
+
+    def v_codes(self) -> torch.Tensor:
+        c = self.cfg
+        n = c.num_heads * c.capacity * c.head_dim
+        return self.buf[self.layout["v"]:self.layout["v"] + n].view(c.num_heads, c.capacity, c.head_dim)
+
+    def positions(self) -> torch.Tensor:
+        c = self.cfg
+        return self.buf[self.layout["pos"]:self.layout["pos"] + 4 * c.capacity].view(torch.int32)
+
+    def scales(self) -> torch.Tensor:
+        c = self.cfg
+        return self.buf[self.layout["scales"]:self.layout["scales"] + 16 * c.num_heads].view(torch.float32).view(4, c.num_heads)

@@ -1,0 +1,76 @@
+"""The per-step sweep: many independent ring caches, each written and attended
+once per diffusion step, in order, on one stream.
+
+One step of the production model is 60 blocks x 4 denoising passes = 240
+attention calls, and each call reads its own cache of 5,788 slots with 757 new
+tokens (Runway Characters post, "Where the Time Went"). Calls are issued one
+after another because in the model each block depends on the previous one.
+
+Inputs are drawn on the device from per-cache seeded generators (seed
+``spec.seed * 1000 + cache index``) with the production-call distribution.
+Every cache is calibrated on its first frame and prefilled with
+``spec.prefill_frames`` frames, so the ring has wrapped before the first timed
+step. A timed step writes each cache's step frame at the next positions and
+attends its queries over the whole ring.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, List
+
+import torch
+
+from . import workloads as W
+
+
+class Sweep:
+    def __init__(self, sfkv, n_caches: int = W.CALLS_PER_STEP, spec: W.WorkloadSpec = W.SWEEP,
+                 keep_frames_of: Iterable[int] = (), device: str = "cuda"):
+        s = spec.shape
+        self.spec = spec
+        self.sfkv = sfkv
+        self.n = s.new_tokens
+        self.rope = sfkv.Rope(s.head_dim, s.max_position, s.rope_base, device=device)
+        self.caches = [sfkv.RingCache(self.rope, s.heads, s.capacity, s.new_tokens, device=device)
+                       for _ in range(n_caches)]
+        need = self.caches[0].workspace_bytes(self.n)
+        # one workspace serves every call: the calls are ordered on one stream
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        self.outs = [torch.empty(self.n, s.heads, s.head_dim, dtype=torch.float32, device=device)
+                     for _ in range(n_caches)]
+        self.gens = [W.FrameStream(spec, seed=spec.seed * 1000 + i, device=device)
+                     for i in range(n_caches)]
+        self.keep = set(keep_frames_of)
+        self.kept: Dict[int, List] = {i: [] for i in self.keep}
+        self.frames = [None] * n_caches
+
+    def _draw(self, i):
+        q, k, v = self.gens[i].frame(self.n)
+        if i in self.keep:
+            self.kept[i].append((q.cpu(), k.cpu(), v.cpu()))
+        return q, k, v
+
+    def prefill(self):
+        """Calibrate each cache on its first frame, write the prefill frames, then
+        draw (and keep resident) the frame every timed step writes."""
+        for i, c in enumerate(self.caches):
+            for f in range(self.spec.prefill_frames):
+                q, k, v = self._draw(i)
+                if f == 0:
+                    c.calibrate_scales(k, v)
+                c.cache_write(k, v)
+            self.frames[i] = self._draw(i)
+
+    def positions_left(self) -> int:
+        st = self.caches[0].state()
+        return (self.rope.max_position - st["next_pos"]) // self.n
+
+    def step(self, stream=None):
+        """One diffusion step: write + attend on every cache, in order."""
+        for c, (q, k, v), out in zip(self.caches, self.frames, self.outs):
+            c.cache_write(k, v, stream)
+            self.sfkv.attend(c.handle, q, out, self.workspace, stream)
+
+    def reset_all(self, stream=None):
+        """Position reset of every cache: one delta rotation each (to position 0)."""
+        for c in self.caches:
+            c.rebase_positions(c.state()["next_pos"], stream)

@@ -1,0 +1,111 @@
+"""Shared pieces of the GPU parity tests: a GPU cache driven in lockstep with its
+oracle twin, and the attention error metric.
+
+Parity bar (fixed here, used by every GPU test):
+  * FP8 code bytes, ring positions, scales and ring counters: bit-exact;
+  * attention, per call over the checked rows: max|o - r| / max|r| <= 2e-2 and
+    mean|o - r| / mean|r| <= 1e-3, where r is the oracle's fp64 attention fed the
+    GPU's own FP8 cache and scales.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import e4m3
+from oracle.cache import RingCache as OracleCache, softmax_attention
+
+A_MAX = 2e-2
+B_MEAN = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def attention_error(out: np.ndarray, ref: np.ndarray):
+    err = np.abs(out.astype(np.float64) - ref)
+    return float(err.max() / np.abs(ref).max()), float(err.mean() / np.abs(ref).mean())
+
+
+class Mirror:
+    """One GPU ring cache and an oracle cache over a subset of its heads."""
+
+    def __init__(self, sfkv, rope, spec, heads=None, max_new=None):
+        s = spec.shape
+        self.spec = spec
+        self.H, self.d, self.C = s.heads, s.head_dim, s.capacity
+        self.heads = list(range(s.heads)) if heads is None else list(heads)
+        max_new = max_new or s.new_tokens
+        self.gpu = sfkv.RingCache(rope, s.heads, s.capacity, max_new)
+        self.ora = OracleCache(len(self.heads), s.head_dim, s.capacity, max_new, s.rope_base,
+                               rope.max_position)
+
+    def _sub(self, t):
+        return t[:, self.heads, :].float().numpy()
+
+    def calibrate(self, k, v):
+        self.gpu.calibrate_scales(k.cuda(), v.cuda())
+        self.ora.calibrate(self._sub(k), self._sub(v))
+
+    def write(self, k, v):
+        self.gpu.cache_write(k.cuda(), v.cuda())
+        self.ora.write(self._sub(k), self._sub(v))
+
+    def rebase(self, delta):
+        self.gpu.rebase_positions(delta)
+        self.ora.rebase(delta)
+
+    def check_cache(self, tag=""):
+        torch.cuda.synchronize()
+        st = self.gpu.state()
+        assert st == {"tokens": self.ora.tokens, "next_pos": self.ora.next_pos,
+                      "write_slot": self.ora.write_slot, "n_valid": self.ora.n_valid}, tag
+        hs = torch.tensor(self.heads)
+        k8 = self.gpu.k_codes()[hs].cpu().numpy()
+        v8 = self.gpu.v_codes()[hs].cpu().numpy()
+        nv = self.ora.n_valid
+        bad_k = np.count_nonzero(k8[:, :nv] != self.ora.k[:, :nv])
+        bad_v = np.count_nonzero(v8[:, :nv] != self.ora.v[:, :nv])
+        assert bad_k == 0 and bad_v == 0, f"{tag}: {bad_k} K and {bad_v} V code bytes differ"
+        pos = self.gpu.positions().cpu().numpy()
+        assert np.array_equal(pos[:nv], self.ora.pos[:nv]), f"{tag}: positions differ"
+        sc = self.gpu.scales()[:, hs].cpu().numpy()
+        assert np.array_equal(sc, self.ora.scales()), f"{tag}: scales differ"
+
+    def reference_from_gpu_cache(self, q, rows):
+        """Oracle attention over the GPU's own codes and scales (checked heads)."""
+        hs = torch.tensor(self.heads)
+        nv = self.ora.n_valid
+        k8 = self.gpu.k_codes()[hs, :nv].cpu().numpy()
+        v8 = self.gpu.v_codes()[hs, :nv].cpu().numpy()
+        sc = self.gpu.scales()[:, hs].cpu().numpy().astype(np.float64)
+        kk = e4m3.decode(k8) * sc[0][:, None, None]
+        vv = e4m3.decode(v8) * sc[2][:, None, None]
+        qr = self.ora.rotated_queries(self._sub(q))[rows]
+        return softmax_attention(qr, kk, vv)
+
+    def check_attend(self, q, rows=None, tag=""):
+        out = self.gpu.attend(q.cuda())
+        torch.cuda.synchronize()
+        n = q.shape[0]
+        rows = np.arange(n) if rows is None else np.asarray(rows)
+        got = out[torch.as_tensor(rows)][:, self.heads].cpu().numpy()
+        ref = self.reference_from_gpu_cache(q, rows)
+        a, b = attention_error(got, ref)
+        full = out.cpu().numpy()
+        assert np.isfinite(full).all(), f"{tag}: non-finite attention output"
+        say(f"  {tag}: attention A={a:.2e} B={b:.2e} over {len(rows)} rows x {len(self.heads)} heads")
+        assert a <= A_MAX and b <= B_MEAN, f"{tag}: A={a:.3e} (bar {A_MAX}) B={b:.3e} (bar {B_MEAN})"
+        return out
+
+
+def spread_rows(n, k):
+    """k query rows spread over [0, n), always including the first and last."""
+    if k >= n:
+        return np.arange(n)
+    r = np.unique(np.linspace(0, n - 1, k).round().astype(np.int64))
+    return r

@@ -1,0 +1,95 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, sizes
+its buffers as documented, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfkv.h")
+
+
+@pytest.fixture(scope="module")
+def sfkv():
+    from streaming_fp8_kv_amd import sfkv as lib
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sfkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for call in ("sfkv_cache_init", "sfkv_calibrate_scales", "sfkv_cache_write",
+                 "sfkv_attend", "sfkv_rebase_positions"):
+        assert call in names
+
+
+def test_every_declared_symbol_is_exported(sfkv):
+    names = declared_functions()
+    assert set(names) == set(sfkv.SYMBOLS)
+    lib = ctypes.CDLL(sfkv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_buffer_sizes(sfkv):
+    cfg = sfkv.CacheConfig(24, 128, 5788, 757)
+    plane = 24 * 5788 * 128
+    n = sfkv.cache_bytes(cfg)
+    assert n % 256 == 0
+    assert n >= 2 * plane + 4 * 5788 + 16 * 24
+    assert n < 2 * plane + 4 * 5788 + 16 * 24 + 4 * 256
+    assert sfkv.rope_bytes(128, 65536) == 65537 * 64 * 8
+    assert sfkv.rope_bytes(64, 1024) == 1025 * 32 * 8
+
+
+@pytest.mark.parametrize("cfg", [
+    (0, 128, 64, 16), (1, 96, 64, 16), (1, 128, 0, 1), (1, 128, 64, 0), (1, 128, 64, 65),
+    (4096, 128, 1 << 24, 16),     # a code plane of 2^43 bytes
+])
+def test_bad_configs_size_zero_and_fail_init(sfkv, cfg):
+    c = sfkv.CacheConfig(*cfg)
+    assert sfkv.cache_bytes(c) == 0
+    h = ctypes.c_void_p()
+    st = sfkv._lib.sfkv_cache_init(ctypes.byref(c), None, None, 0, None, ctypes.byref(h))
+    assert st == sfkv.EINVAL and not h.value
+    assert sfkv._lib.sfkv_last_error()
+
+
+@pytest.mark.parametrize("base,d,maxp,ptr,nbytes", [
+    (10000.0, 96, 100, 256, 1 << 20),       # head_dim
+    (10000.0, 128, 0, 256, 1 << 20),        # max_position
+    (1.0, 128, 100, 256, 1 << 20),          # base
+    (float("inf"), 128, 100, 256, 1 << 20),
+    (10000.0, 128, 100, 0, 1 << 20),        # NULL memory
+    (10000.0, 128, 100, 258, 1 << 20),      # misaligned
+    (10000.0, 128, 100, 256, 100),          # too small
+])
+def test_rope_init_validation(sfkv, base, d, maxp, ptr, nbytes):
+    h = ctypes.c_void_p()
+    st = sfkv._lib.sfkv_rope_init(base, d, maxp, ptr or None, nbytes, None, ctypes.byref(h))
+    assert st == sfkv.EINVAL and not h.value
+
+
+def test_null_handles(sfkv):
+    lib = sfkv._lib
+    assert lib.sfkv_cache_write(None, 256, 256, 0, 1, None) == sfkv.EINVAL
+    assert lib.sfkv_calibrate_scales(None, 256, 256, 0, 1, None) == sfkv.EINVAL
+    assert lib.sfkv_attend(None, 256, 0, 1, 256, None, 0, None) == sfkv.EINVAL
+    assert lib.sfkv_rebase_positions(None, 0, None) == sfkv.EINVAL
+    assert lib.sfkv_cache_state(None, None, None, None, None) == sfkv.EINVAL
+    assert lib.sfkv_attend_workspace_bytes(None, 757) == 0
+    assert lib.sfkv_status_string(-3) == b"position out of range"
+
+
+def test_binding_has_no_fallback():
+    src = open(os.path.join(ROOT, "streaming_fp8_kv_amd", "sfkv.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
+    assert "raise ImportError" in src
