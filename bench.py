@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 ring KV-cache path on one MI355X.
+
+A step is one diffusion step of the production model: 240 attention calls
+(60 blocks x 4 passes), each a cache_write of 757 new bf16 tokens followed by
+an attend of those 757 queries over its own 5,788-slot FP8 ring (24 heads x 128
+dims), issued in order on one stream. Every cache is prefilled with 8 frames,
+so the rings have wrapped. Inputs are synthetic, drawn on the device, and are
+resident before the timed region starts.
+
+Prints one JSON line. ``value`` is microseconds per cache_write + attend call
+(step time / 240). ``roofline`` is for attend, the dominant kernel: algorithmic
+FLOPs per launch (4 * n * slots * heads * head_dim) over its average duration
+from HIP events recorded around every attend launch inside the timed region, on
+the stream the kernels run on, against the dense FP8 MFMA peak. The position
+reset (one delta rotation per cache) is timed in a separate region and reported
+under ``extra``. ``cpu_baseline`` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+# MI355X published peaks
+PEAK_FP8_TFLOPS = 5000.0      # dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # HBM3E
+
+# Traffic per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy
+# kernel of known size; None until measured for the current kernel.
+ATTEND_TRAFFIC_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--calls", type=int, default=240, help="caches (calls) per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-calls", type=int, default=2)
+    return ap.parse_args()
+
+
+def cpu_baseline(n_calls: int):
+    """The oracle as it stands, on the host: cache_write + attend of the
+    production call (757 tokens into a wrapped 5,788-slot ring, 24 heads)."""
+    import numpy as np
+    from oracle.cache import RingCache
+    from streaming_fp8_kv_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    spec = W.PROD
+    s = spec.shape
+    fs = W.FrameStream(spec)
+    frames = [tuple(t.float().numpy() for t in fs.frame()) for _ in range(8 + n_calls)]
+    rc = RingCache(s.heads, s.head_dim, s.capacity, s.new_tokens, s.rope_base, s.max_position)
+    rc.calibrate(frames[0][1], frames[0][2])
+    for _, k, v in frames[:8]:
+        rc.write(k, v)                      # prefill (untimed)
+    # RoPE rows of the timed positions are computed once, untimed, as the GPU
+    # path's table is built at set-up
+    from oracle import rope
+    rope.cos_sin(np.arange(rc.next_pos, rc.next_pos + n_calls * s.new_tokens), s.head_dim, s.rope_base)
+    t0 = time.perf_counter()
+    for q, k, v in frames[8:]:
+        rc.write(k, v)
+        rc.attend(q)
+    dt = time.perf_counter() - t0
+    return {"value": dt / n_calls * 1e6, "unit": "us per cache_write+attend call",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{n_calls} production calls (757 new tokens, 5,788-slot wrapped ring, "
+                      f"24 heads x 128, fp64 attention over all rows) after an untimed 8-frame prefill; "
+                      f"{dt:.1f} s of CPU time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from streaming_fp8_kv_amd import sfkv, workloads as W
+    from streaming_fp8_kv_amd.sweep import Sweep
+
+    torch.cuda.set_device(0)
+    spec = W.SWEEP
+    s = spec.shape
+    n_calls = args.calls
+    print(f"# setting up {n_calls} caches", file=sys.stderr, flush=True)
+    sw = Sweep(sfkv, n_caches=n_calls, spec=spec)
+    sw.prefill()
+    torch.cuda.synchronize()
+    if sw.positions_left() < args.warmup + args.steps + 1:
+        raise SystemExit("too many steps for the position range; lower --steps/--warmup")
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sw.step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events around every attend launch ----------
+    E = torch.cuda.Event
+    ev_start, ev_end = E(enable_timing=True), E(enable_timing=True)
+    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps * n_calls)]
+    wr = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps * n_calls)]
+    torch.cuda.synchronize()
+    ev_start.record(stream)
+    j = 0
+    for _ in range(args.steps):
+        for c, (q, k, v), out in zip(sw.caches, sw.frames, sw.outs):
+            wr[j][0].record(stream)
+            sfkv.cache_write(c.handle, k, v, stream)
+            wr[j][1].record(stream)
+            att[j][0].record(stream)
+            sfkv.attend(c.handle, q, out, sw.workspace, stream)
+            att[j][1].record(stream)
+            j += 1
+    ev_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev_start.elapsed_time(ev_end)
+    ms_per_step = total_ms / args.steps
+    attend_us = sum(a.elapsed_time(b) for a, b in att) * 1e3 / len(att)
+    write_us = sum(a.elapsed_time(b) for a, b in wr) * 1e3 / len(wr)
+
+    # ---- position reset: one delta rotation of every cache ------------------
+    rb = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for c, (a, b) in zip(sw.caches, rb):
+        a.record(stream)
+        c.rebase_positions(c.state()["next_pos"], stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    rebase_us = sum(a.elapsed_time(b) for a, b in rb) * 1e3 / len(rb)
+
+    n, H, d, C = s.new_tokens, s.heads, s.head_dim, s.capacity
+    attend_flops = 4.0 * n * C * H * d
+    write_bytes = 2 * n * H * d * 2 + 2 * n * H * d * 1
+    rebase_bytes = 2 * H * C * d
+    achieved = attend_flops / (attend_us * 1e-6) / 1e12
+    line = {
+        "metric": "us per cache_write+attend call at 757x5788 (240-call step)",
+        "value": round(ms_per_step * 1e3 / n_calls, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "calls_per_step": n_calls, "heads": H, "head_dim": d,
+                   "new_tokens": n, "ring_slots": C, "prefill_frames": spec.prefill_frames,
+                   "input_dtype": "bf16", "cache_dtype": "e4m3"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": ATTEND_TRAFFIC_BYTES},
+        "extra": {
+            "attend_us": round(attend_us, 3),
+            "write_us": round(write_us, 3),
+            "write_hbm_frac": round(write_bytes / (write_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "rebase_us_per_cache": round(rebase_us, 3),
+            "rebase_hbm_frac": round(rebase_bytes / (rebase_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "reset_step_extra_ms": round(rebase_us * n_calls / 1e3, 4),
+            "attend_splits": sfkv._lib and None,
+        },
+    }
+    line["extra"].pop("attend_splits")
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_sample_calls)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -130,14 +130,17 @@ sfkv_status sfkv_cache_write(sfkv_cache *cache, const void *k, const void *v,
  * positions inside the kernel. Keys and values are the decoded FP8 codes times
  * the head's scale. Slot order does not matter because every key carries its
  * own rotation. Output is fp32 [n_q][H][d].
- * `workspace` is device memory of at least sfkv_attend_workspace_bytes(cache,
- * n_q) bytes (may be NULL when that is 0); calls on one stream may share it.
+ * `workspace` is device memory (256-byte aligned) of at least
+ * sfkv_attend_workspace_bytes(cache) bytes, or NULL when that is 0. The size
+ * depends only on the cache configuration and serves every n_q up to
+ * max_new_tokens (no buffer per token count); calls ordered on one stream may
+ * share one workspace, calls that overlap on different streams may not.
  * Errors: EINVAL (pointers, dtype, n_q mismatch, workspace too small),
  *         ESTATE (no write yet).
  * Source: "Where the Time Went" (the call's attention over its whole cache);
  * "Blackwell and Beyond Four GPUs" (FP8 attention taking per-head scales);
  * "Do It Once, at Write Time" (time-order positions once the ring wraps). */
-size_t sfkv_attend_workspace_bytes(const sfkv_cache *cache, int32_t n_q);
+size_t sfkv_attend_workspace_bytes(const sfkv_cache *cache);
 sfkv_status sfkv_attend(sfkv_cache *cache, const void *q, sfkv_dtype dtype, int32_t n_q,
                         float *out, void *workspace, size_t workspace_bytes, void *stream);
 

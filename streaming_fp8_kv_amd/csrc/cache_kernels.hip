@@ -75,13 +75,13 @@ __device__ inline float scaled(float x, float inv) {
   return x * inv;
 }
 
-// One thread = 8 consecutive dims of one (token, head): 16 B of bf16 K and V
-// in, 8 B of K codes and 8 B of V codes out. Consecutive threads walk the dims
-// of a head, then the heads of a token, so the reads are fully coalesced and
-// every 128-byte row of a code plane is written by 16 adjacent lanes.
+// One thread = 16 consecutive dims of one (token, head): 32 B of bf16 K and of V
+// in, 16 B of K codes and 16 B of V codes out. Consecutive threads walk the
+// dims of a head, then the heads of a token, so the reads are fully coalesced
+// and each 128-byte row of a code plane is written by 8 adjacent lanes.
 __global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
   // 32-bit indexing: the host keeps every code plane below 2^31 bytes.
-  const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 3;
+  const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 4;
   const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
   const unsigned total = static_cast<unsigned>(a.n) * a.heads * chunks;
   if (idx >= total) return;
@@ -93,31 +93,37 @@ __global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
   int slot = a.slot0 + i;
   if (slot >= a.capacity) slot -= a.capacity;   // n <= capacity, so one wrap at most
   const int p = a.pos0 + i;
-  const size_t in_elem = (static_cast<size_t>(i) * a.heads + h) * a.head_dim + c * 8;
-  const size_t out_off = (static_cast<size_t>(h) * a.capacity + slot) * a.head_dim + c * 8;
+  const size_t in_elem = (static_cast<size_t>(i) * a.heads + h) * a.head_dim + c * 16;
+  const size_t out_off = (static_cast<size_t>(h) * a.capacity + slot) * a.head_dim + c * 16;
 
   const float inv_k = a.scales[a.heads + h];
   const float inv_v = a.scales[3 * a.heads + h];
 
-  float x[8];
+  float x[16];
   load8(a.k, in_elem, a.dtype, x);
-  const RopePair *row = a.rope + static_cast<size_t>(p) * (a.head_dim >> 1) + c * 4;
-  const float4 cs01 = *reinterpret_cast<const float4 *>(row);
-  const float4 cs23 = *reinterpret_cast<const float4 *>(row + 2);
-  rotate_pair(x[0], x[1], RopePair{cs01.x, cs01.y});
-  rotate_pair(x[2], x[3], RopePair{cs01.z, cs01.w});
-  rotate_pair(x[4], x[5], RopePair{cs23.x, cs23.y});
-  rotate_pair(x[6], x[7], RopePair{cs23.z, cs23.w});
-  uint2 kw;
+  load8(a.k, in_elem + 8, a.dtype, x + 8);
+  const float4 *row = reinterpret_cast<const float4 *>(a.rope + static_cast<size_t>(p) * (a.head_dim >> 1) + c * 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 cs = row[j];
+    rotate_pair(x[4 * j], x[4 * j + 1], RopePair{cs.x, cs.y});
+    rotate_pair(x[4 * j + 2], x[4 * j + 3], RopePair{cs.z, cs.w});
+  }
+  uint4 kw;
   kw.x = encode4(scaled(x[0], inv_k), scaled(x[1], inv_k), scaled(x[2], inv_k), scaled(x[3], inv_k));
   kw.y = encode4(scaled(x[4], inv_k), scaled(x[5], inv_k), scaled(x[6], inv_k), scaled(x[7], inv_k));
-  *reinterpret_cast<uint2 *>(a.k8 + out_off) = kw;
+  kw.z = encode4(scaled(x[8], inv_k), scaled(x[9], inv_k), scaled(x[10], inv_k), scaled(x[11], inv_k));
+  kw.w = encode4(scaled(x[12], inv_k), scaled(x[13], inv_k), scaled(x[14], inv_k), scaled(x[15], inv_k));
+  *reinterpret_cast<uint4 *>(a.k8 + out_off) = kw;
 
   load8(a.v, in_elem, a.dtype, x);
-  uint2 vw;
+  load8(a.v, in_elem + 8, a.dtype, x + 8);
+  uint4 vw;
   vw.x = encode4(scaled(x[0], inv_v), scaled(x[1], inv_v), scaled(x[2], inv_v), scaled(x[3], inv_v));
   vw.y = encode4(scaled(x[4], inv_v), scaled(x[5], inv_v), scaled(x[6], inv_v), scaled(x[7], inv_v));
-  *reinterpret_cast<uint2 *>(a.v8 + out_off) = vw;
+  vw.z = encode4(scaled(x[8], inv_v), scaled(x[9], inv_v), scaled(x[10], inv_v), scaled(x[11], inv_v));
+  vw.w = encode4(scaled(x[12], inv_v), scaled(x[13], inv_v), scaled(x[14], inv_v), scaled(x[15], inv_v));
+  *reinterpret_cast<uint4 *>(a.v8 + out_off) = vw;
 
   if (h == 0 && c == 0) a.pos[slot] = p;
 }
@@ -207,7 +213,7 @@ inline unsigned blocks_for(size_t threads, unsigned per_block) {
 }  // namespace
 
 hipError_t launch_write(const WriteLaunch &a, hipStream_t s) {
-  const size_t threads = static_cast<size_t>(a.n) * a.heads * (a.head_dim >> 3);
+  const size_t threads = static_cast<size_t>(a.n) * a.heads * (a.head_dim >> 4);
   hipLaunchKernelGGL(write_kernel, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -252,16 +252,23 @@ static int n_valid_of(const sfkv_cache *c) {
   return static_cast<int>(c->tokens < c->cfg.capacity ? c->tokens : c->cfg.capacity);
 }
 
-static size_t attend_ws_bytes(const sfkv_cache_cfg &cfg, int splits, int32_t n_q) {
-  if (splits <= 1) return 0;
-  const size_t rows = static_cast<size_t>(splits) * n_q * cfg.num_heads;
+// Partial results of split-KV attention: O rows [splits][n_q][heads][head_dim]
+// fp32, then (max, sum) pairs. The workspace is sized once per cache for its
+// largest write; a call with fewer queries caps its split count to fit, so one
+// buffer serves every token count.
+static size_t attend_rows_capacity(const sfkv_cache_cfg &cfg) {
+  const int s = sfkv::attend_splits(cfg.max_new_tokens, cfg.num_heads, cfg.capacity);
+  return s > 1 ? static_cast<size_t>(s) * cfg.max_new_tokens * cfg.num_heads : 0;
+}
+
+static size_t attend_ws_bytes(const sfkv_cache_cfg &cfg, size_t rows) {
+  if (rows == 0) return 0;
   return align_up(rows * cfg.head_dim * sizeof(float), 256) + align_up(rows * 2 * sizeof(float), 256);
 }
 
-size_t sfkv_attend_workspace_bytes(const sfkv_cache *c, int32_t n_q) {
-  if (!c || n_q < 1 || n_q > c->cfg.max_new_tokens) return 0;
-  const int s = sfkv::attend_splits(n_q, c->cfg.num_heads, c->cfg.capacity);
-  return attend_ws_bytes(c->cfg, s, n_q);
+size_t sfkv_attend_workspace_bytes(const sfkv_cache *c) {
+  if (!c) return 0;
+  return attend_ws_bytes(c->cfg, attend_rows_capacity(c->cfg));
 }
 
 sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t n_q, float *out,
@@ -273,10 +280,17 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
   const int nv = n_valid_of(c);
-  const int splits = sfkv::attend_splits(n_q, c->cfg.num_heads, nv);
-  const size_t need = attend_ws_bytes(c->cfg, splits, n_q);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
-    return fail(SFKV_EINVAL, "workspace missing, smaller than sfkv_attend_workspace_bytes() or not 256-byte aligned");
+  const size_t rows_cap = attend_rows_capacity(c->cfg);
+  const size_t rows_per_split = static_cast<size_t>(n_q) * c->cfg.num_heads;
+  int splits = sfkv::attend_splits(n_q, c->cfg.num_heads, nv);
+  if (splits > 1 && static_cast<size_t>(splits) * rows_per_split > rows_cap)
+    splits = static_cast<int>(rows_cap / rows_per_split);
+  if (splits < 2) splits = 1;
+  if (splits > 1) {
+    const size_t need = attend_ws_bytes(c->cfg, rows_cap);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+      return fail(SFKV_EINVAL, "workspace missing, smaller than sfkv_attend_workspace_bytes() or not 256-byte aligned");
+  }
   sfkv::AttendLaunch a;
   a.q = q;
   a.dtype = dtype;
@@ -295,10 +309,9 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   a.part_o = nullptr;
   a.part_ml = nullptr;
   if (splits > 1) {
-    const size_t rows = static_cast<size_t>(splits) * n_q * c->cfg.num_heads;
     a.part_o = static_cast<float *>(workspace);
     a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
-                                          align_up(rows * c->cfg.head_dim * sizeof(float), 256));
+                                          align_up(rows_cap * c->cfg.head_dim * sizeof(float), 256));
   }
   return launched(sfkv::launch_attend(a, as_stream(stream)));
 }

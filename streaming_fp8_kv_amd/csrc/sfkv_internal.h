@@ -57,7 +57,7 @@ hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s);
 hipError_t launch_attend(const AttendLaunch &a, hipStream_t s);
 
 // Attention tiling shared by the launcher and the workspace sizing.
-constexpr int kAttendQueriesPerBlock = 64;
+constexpr int kAttendQueriesPerBlock = 128;  // 4 waves x 32 queries
 constexpr int kAttendKeysPerTile = 64;
 int attend_splits(int n_q, int heads, int capacity);
 

@@ -63,7 +63,7 @@ _sig("sfkv_cache_init", ctypes.c_int, _P(CacheConfig), _vp, _vp, _sz, _vp, _P(_v
 _sig("sfkv_cache_destroy", None, _vp)
 _sig("sfkv_calibrate_scales", ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i32, _vp)
 _sig("sfkv_cache_write", ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i32, _vp)
-_sig("sfkv_attend_workspace_bytes", _sz, _vp, _i32)
+_sig("sfkv_attend_workspace_bytes", _sz, _vp)
 _sig("sfkv_attend", ctypes.c_int, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
 _sig("sfkv_rebase_positions", ctypes.c_int, _vp, _i64, _vp)
 _sig("sfkv_cache_state", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i32), _P(_i32))
@@ -136,8 +136,8 @@ def cache_write(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
                                  k.shape[0], _stream(stream)))
 
 
-def attend_workspace_bytes(handle: int, n_q: int) -> int:
-    return int(_lib.sfkv_attend_workspace_bytes(handle, n_q))
+def attend_workspace_bytes(handle: int) -> int:
+    return int(_lib.sfkv_attend_workspace_bytes(handle))
 
 
 def attend(handle: int, q: torch.Tensor, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
@@ -211,15 +211,15 @@ class RingCache:
         cache_write(self.handle, _frame(k, self.cfg.num_heads, self.cfg.head_dim),
                     _frame(v, self.cfg.num_heads, self.cfg.head_dim), stream)
 
-    def workspace_bytes(self, n_q: int) -> int:
-        return attend_workspace_bytes(self.handle, n_q)
+    def workspace_bytes(self) -> int:
+        return attend_workspace_bytes(self.handle)
 
     def attend(self, q, out=None, workspace=None, stream=None):
         q = _frame(q, self.cfg.num_heads, self.cfg.head_dim)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         if workspace is None:
-            need = self.workspace_bytes(q.shape[0])
+            need = self.workspace_bytes()
             if need:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         attend(self.handle, q, out, workspace, stream)

@@ -32,7 +32,7 @@ class Sweep:
         self.rope = sfkv.Rope(s.head_dim, s.max_position, s.rope_base, device=device)
         self.caches = [sfkv.RingCache(self.rope, s.heads, s.capacity, s.new_tokens, device=device)
                        for _ in range(n_caches)]
-        need = self.caches[0].workspace_bytes(self.n)
+        need = self.caches[0].workspace_bytes()
         # one workspace serves every call: the calls are ordered on one stream
         self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
         self.outs = [torch.empty(self.n, s.heads, s.head_dim, dtype=torch.float32, device=device)
