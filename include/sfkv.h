@@ -131,12 +131,13 @@ sfkv_status sfkv_cache_write(sfkv_cache *cache, const void *k, const void *v,
  * the head's scale. Slot order does not matter because every key carries its
  * own rotation. Output is fp32 [n_q][H][d].
  * `workspace` is device memory (256-byte aligned) of at least
- * sfkv_attend_workspace_bytes(cache) bytes, or NULL when that is 0. The size
- * depends only on the cache configuration and serves every n_q up to
- * max_new_tokens (no buffer per token count); calls ordered on one stream may
- * share one workspace, calls that overlap on different streams may not.
- * Errors: EINVAL (pointers, dtype, n_q mismatch, workspace too small),
- *         ESTATE (no write yet).
+ * sfkv_attend_workspace_bytes(cache) bytes; it holds the prepared query terms
+ * and split partials of one call. The size depends only on the cache
+ * configuration and serves every n_q up to max_new_tokens (no buffer per token
+ * count); calls ordered on one stream may share one workspace, calls that
+ * overlap on different streams may not.
+ * Errors: EINVAL (pointers, dtype, n_q mismatch, workspace missing or too
+ *         small), ESTATE (no write yet).
  * Source: "Where the Time Went" (the call's attention over its whole cache);
  * "Blackwell and Beyond Four GPUs" (FP8 attention taking per-head scales);
  * "Do It Once, at Write Time" (time-order positions once the ring wraps). */

@@ -7,22 +7,25 @@
 // recomputed for cached keys ("Do It Once, at Write Time"). Queries are
 // rotated here, at the positions of the write they belong to.
 //
-// Data path per workgroup (one head, 64 queries, one key range):
-//   * queries: bf16 -> fp32 RoPE -> times scale_k * log2(e) / sqrt(d) -> three
-//     E4M3 terms, each with one power-of-two (E8M0) scale per 32 head dims;
-//     kept in registers as the B operand of the block-scaled FP8 MFMA;
+// Data path per workgroup (one head, 128 queries = 4 waves x 32, one key range):
+//   * queries (a small kernel of their own, once per call): bf16 -> fp32 RoPE ->
+//     times scale_k * log2(e) / sqrt(d) -> three E4M3 terms, each with one
+//     power-of-two (E8M0) scale per 32 head dims; each wave keeps its 32
+//     queries' terms in registers as the B operand of the block-scaled FP8
+//     MFMA 32x32x64;
 //   * keys: raw E4M3 codes staged in LDS, fed unconverted as the A operand, so
-//     one MFMA 16x16x128 per term computes 16 keys x 16 queries over the head;
-//   * scores come out transposed (keys x queries) and already in log2 units;
-//     online softmax per query column with exp2, wavefront reductions over the
-//     four lanes that share a column;
-//   * P is rounded to fp16 (round to nearest even) and stays in registers as
-//     the B operand of the fp16 MFMA 16x16x32; V is staged in LDS once per tile,
-//     converted E4M3 -> fp16 (exact) and transposed to [dim][key];
-//   * O^T accumulates in fp32; the scale_v / sum division happens once at the end.
-// A three-term query carries about 12 significant bits and fp16 P about 11, which
-// is what keeps the result within 1e-3 mean relative error of exact attention on
-// the same FP8 cache; two-term or single-FP8 queries do not.
+//     each MFMA computes 32 keys x 32 queries over 64 head dims;
+//   * scores come out transposed (keys x queries), in log2 units and already
+//     shifted by the column's reference max; P = exp2(S) in fp16 stays in
+//     registers as the B operand of the fp16 MFMA 32x32x16;
+//   * V is staged in LDS once per tile, converted E4M3 -> fp16 (exact) and
+//     transposed to [dim][key]; O^T accumulates in fp32 and the scale_v / sum
+//     division happens once at the end.
+// A three-term query carries about 12 significant bits and fp16 P about 11,
+// which keeps the result within 1e-3 mean relative error of exact attention on
+// the same FP8 cache; two-term or single-FP8 queries do not. The 32x32 MFMA
+// shapes are the ones that run at full rate on gfx950 (the 16x16 fp16 shape
+// runs at half rate).
 //
 // Long key ranges are split across workgroups (split-KV) to fill the 256 CUs; a
 // second kernel merges the partial (max, sum, O) triples.
@@ -35,18 +38,21 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int BK = kAttendKeysPerTile;      // 64 keys per LDS tile
 constexpr int KSTRIDE = 144;                // bytes per key row in LDS (128 + 16 pad)
-// V^T tile in LDS: one 128-byte row per head dim, 16 slots of 4 keys (8 bytes);
-// slot j of row d lives at j ^ vswz(d), which keeps both the transposing stores
-// (rows 8 apart) and the MFMA fragment reads (16 consecutive rows) free of bank
-// conflicts.
+// V^T tile in LDS: one 128-byte row per head dim holding 64 keys as 4 groups of
+// 16. Inside a group, key k sits at position 8*bit2(k) + 4*bit3(k) + (k & 3), so
+// the 8 keys one lane of the PV MFMA needs are contiguous (one 16-byte read),
+// and the 16-byte slot s of row d is stored at slot s ^ vswz(d). The swizzle
+// keeps the fragment reads (8 consecutive rows per cycle) free of bank
+// conflicts and the transposing 8-byte stores at most 2-way.
 constexpr int VROW = 64;                    // halfs per dim row (64 keys)
-__device__ __forceinline__ int vswz(int row) { return (row ^ (row >> 3)) & 15; }
+__device__ __forceinline__ int vswz(int row) { return (row ^ (row >> 3)) & 7; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 
@@ -99,53 +105,50 @@ __device__ inline void decode16(const int *w, float *x) {
   }
 }
 
-// Q terms of one 16-query block for one lane (query column r, lane group g):
-// bytes 0..15 of each term -> head dims [16g, 16g+16), bytes 16..31 -> [64+16g,
-// 64+16g+16) (the lane layout of the 16x16x128 block-scaled MFMA). The 32-dim
-// scale block b is shared by lanes g = 2(b%2) and 2(b%2)+1 and its E8M0 scale is
-// supplied by lane g = b.
+// Query preparation, one thread per (query, head, 32-dim block): RoPE at the
+// query's position, the factor scale_k * log2(e) / sqrt(d) folded in, then three
+// E4M3 terms, each the rounding of what the previous terms left over, with one
+// power-of-two (E8M0) scale per term for the block. Codes are stored in natural
+// dim order, [query][head][term][dim]; the scale bytes of terms 0..2 are packed
+// into one word per block. A 32-dim block is exactly one scale block of the
+// 32x32x64 block-scaled MFMA.
 template <int D>
-__device__ inline void query_terms(const AttendLaunch &a, int h, int qi, int g, int r, v8i qt[3],
-                                   int &qscale) {
+__global__ __launch_bounds__(256) void query_prep_kernel(AttendLaunch a) {
+  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int NB = D / 32;
+  if (idx >= static_cast<unsigned>(a.n_q) * a.heads * NB) return;
+  const int b = idx % NB;
+  const unsigned qh = idx / NB;                 // qi * heads + h
+  const int h = qh % a.heads;
+  const int qi = qh / a.heads;
   float x[32];
-  const bool has2 = (64 + 16 * g) < D;
+  const size_t base = static_cast<size_t>(qh) * D + 32 * b;
+  load16(a.q, base, a.dtype, x);
+  load16(a.q, base + 16, a.dtype, x + 16);
+  // A rebase can leave the last write's queries at negative positions;
+  // cos(-x) = cos(x) and sin(-x) = -sin(x) reuse the row of |p|.
+  const int qp = a.qpos0 + qi;
+  const float sgn = qp < 0 ? -1.0f : 1.0f;
+  const RopePair *row = a.rope + static_cast<size_t>(qp < 0 ? -qp : qp) * (D / 2) + 16 * b;
+  const float qs = a.scales[h] * kLog2e * (1.0f / sqrtf(static_cast<float>(D)));
 #pragma unroll
-  for (int j = 0; j < 32; ++j) x[j] = 0.0f;
-  if (qi < a.n_q) {
-    const size_t base = (static_cast<size_t>(qi) * a.heads + h) * D;
-    // A rebase can leave the last write's queries at negative positions;
-    // cos(-x) = cos(x) and sin(-x) = -sin(x) reuse the row of |p|.
-    const int qp = a.qpos0 + qi;
-    const float sgn = qp < 0 ? -1.0f : 1.0f;
-    const RopePair *row = a.rope + static_cast<size_t>(qp < 0 ? -qp : qp) * (D / 2);
-    load16(a.q, base + 16 * g, a.dtype, x);
-    if (has2) load16(a.q, base + 64 + 16 * g, a.dtype, x + 16);
-    const float qs = a.scales[h] * kLog2e * (1.0f / sqrtf(static_cast<float>(D)));
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (half == 1 && !has2) break;
-      const int pair0 = half == 0 ? 8 * g : 32 + 8 * g;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        RopePair cs = row[pair0 + j];
-        cs.s *= sgn;
-        float u = x[16 * half + 2 * j], v = x[16 * half + 2 * j + 1];
-        x[16 * half + 2 * j] = (u * cs.c - v * cs.s) * qs;
-        x[16 * half + 2 * j + 1] = (u * cs.s + v * cs.c) * qs;
-      }
-    }
+  for (int j = 0; j < 16; ++j) {
+    RopePair cs = row[j];
+    cs.s *= sgn;
+    const float u = x[2 * j], v = x[2 * j + 1];
+    x[2 * j] = (u * cs.c - v * cs.s) * qs;
+    x[2 * j + 1] = (u * cs.s + v * cs.c) * qs;
   }
+  uint32_t packed = 0;
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
-    float m0 = 0.0f, m1 = 0.0f;
+    float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) { m0 = fmaxf(m0, fabsf(x[j])); m1 = fmaxf(m1, fabsf(x[16 + j])); }
-    m0 = fmaxf(m0, __shfl_xor(m0, 16));
-    m1 = fmaxf(m1, __shfl_xor(m1, 16));
-    const int e0 = block_exponent(m0), e1 = block_exponent(m1);
+    for (int j = 0; j < 32; ++j) m = fmaxf(m, fabsf(x[j]));
+    const int e = block_exponent(m);
     float y[32];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) { y[j] = ldexpf(x[j], -e0); y[16 + j] = ldexpf(x[16 + j], -e1); }
+    for (int j = 0; j < 32; ++j) y[j] = ldexpf(x[j], -e);
     int w[8];
     encode16(y, w);
     encode16(y + 16, w + 4);
@@ -153,29 +156,76 @@ __device__ inline void query_terms(const AttendLaunch &a, int h, int qi, int g, 
     decode16(w, dq);
     decode16(w + 4, dq + 16);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) { x[j] -= ldexpf(dq[j], e0); x[16 + j] -= ldexpf(dq[16 + j], e1); }
+    for (int j = 0; j < 32; ++j) x[j] -= ldexpf(dq[j], e);
+    uint4 *dst = reinterpret_cast<uint4 *>(a.qterm + (static_cast<size_t>(qh) * 3 + t) * D + 32 * b);
+    dst[0] = uint4{static_cast<uint32_t>(w[0]), static_cast<uint32_t>(w[1]), static_cast<uint32_t>(w[2]), static_cast<uint32_t>(w[3])};
+    dst[1] = uint4{static_cast<uint32_t>(w[4]), static_cast<uint32_t>(w[5]), static_cast<uint32_t>(w[6]), static_cast<uint32_t>(w[7])};
+    packed |= static_cast<uint32_t>(127 + e) << (8 * t);
+  }
+  a.qscale[static_cast<size_t>(qh) * NB + b] = packed;
+}
+
+// Q terms of one lane of a 32-query block (column r = lane & 31, half
+// hh = lane >> 5), for the two 64-dim halves dh of the head. In the 32x32x64
+// block-scaled MFMA a lane's 32 bytes are dims 64dh + [16hh, 16hh+16) (bytes
+// 0..15) and 64dh + 32 + [16hh, 16hh+16) (bytes 16..31); the scale of 32-dim
+// block hh of dh comes from this lane. Rows past n_q load as zero terms.
+template <int D>
+__device__ inline void load_query_terms(const AttendLaunch &a, int h, int qi, int hh, v8i qt[D / 64][3],
+                                        int qscale[D / 64]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qt[t][j] = w[j];
-    // lanes 0 and 3 hold the scale they supply; lanes 1 and 2 swap theirs
-    const int send = (g & 1) ? e1 : e0;
-    const int src = r + 16 * (g == 1 ? 2 : (g == 2 ? 1 : g));
-    qscale |= (127 + __shfl(send, src)) << (8 * t);   // byte t: E8M0 scale of term t
+  for (int dh = 0; dh < D / 64; ++dh) {
+    qscale[dh] = 0x7f7f7f;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) qt[dh][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  if (qi >= a.n_q) return;
+  const size_t qh = static_cast<size_t>(qi) * a.heads + h;
+#pragma unroll
+  for (int dh = 0; dh < D / 64; ++dh) {
+    qscale[dh] = static_cast<int>(a.qscale[qh * (D / 32) + 2 * dh + hh]);
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const uint8_t *src = a.qterm + (qh * 3 + t) * D + 64 * dh + 16 * hh;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(src);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(src + 32);
+      qt[dh][t] = v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                      static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    }
   }
 }
 
-// QB query blocks of 16 per wave, 4 waves per workgroup. The next key tile is
-// loaded into registers while the current one is consumed from LDS. The grid is
-// one-dimensional and remapped so that all query tiles of one (head, key range)
-// run on the same XCD and share its L2 (workgroups are dealt to the 8 XCDs
-// round-robin).
-template <int D, int QB>
+// A pointer the compiler can keep in scalar registers.
+__device__ __forceinline__ void *uniform_ptr(const void *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// One wave = one block of 32 queries, 4 waves per workgroup; a tile is 64 keys
+// = two blocks of 32. The loop is software-pipelined by block: the QK MFMAs of
+// the next block are issued before the softmax of the current one, so the
+// matrix core works while the vector ALU computes exponentials. Tiles go
+// through three LDS buffers (the next tile is stored while the current one and
+// the first block of the following one are read); the tile after that is
+// loaded into registers meanwhile. The grid is one-dimensional and remapped so
+// that all query tiles of one (head, key range) run on the same XCD and share
+// its L2 (workgroups are dealt to the 8 XCDs round-robin).
+template <int D>
 __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  constexpr int BQW = 16 * QB;       // queries per wave
-  constexpr int BQB = 4 * BQW;       // queries per workgroup
-  constexpr float kPmax = 32768.0f;  // P stays below 2^15, well inside fp16
-  __shared__ __attribute__((aligned(16))) uint8_t sK[BK * KSTRIDE];
-  __shared__ __attribute__((aligned(16))) _Float16 sVt[D * VROW];
+  constexpr int DH = D / 64;          // 64-dim halves of the head
+  constexpr int BQB = 128;            // queries per workgroup
+  constexpr float kShiftAt = 15.0f;   // P = exp2(s - m_ref) stays <= 2^15, inside fp16
+  __shared__ __attribute__((aligned(16))) uint8_t sK[3][BK * KSTRIDE];
+  __shared__ __attribute__((aligned(16))) _Float16 sVt[3][D * VROW];
 
   const int tiles_q = (a.n_q + BQB - 1) / BQB;
   const int n_blocks = tiles_q * a.heads * a.splits;
@@ -189,50 +239,63 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, g = lane >> 4;
+  const int r = lane & 31, hh = lane >> 5;
   const int H = a.heads;
-  const int q0 = qtile * BQB + wave * BQW;
+  const int qi = qtile * BQB + wave * 32 + r;      // this lane's query column
 
-  v8i qt[QB][3];
-  int qscale[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qscale[qb] = 0;
-    query_terms<D>(a, h, q0 + 16 * qb + r, g, r, qt[qb], qscale[qb]);
-  }
+  v8i qt[DH][3];
+  int qscale[DH];
+  load_query_terms<D>(a, h, qi, hh, qt, qscale);
 
   const int per_split = ((a.n_valid + a.splits - 1) / a.splits + BK - 1) / BK * BK;
   const int kbeg = split * per_split;
   const int kend = min(a.n_valid, kbeg + per_split);
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const uint8_t *kplane = a.k8 + static_cast<size_t>(h) * a.capacity * D;
   const uint8_t *vplane = a.v8 + static_cast<size_t>(h) * a.capacity * D;
 
-  // staging roles: K = 16-byte chunks (8 per 128-byte row); V = 4 keys x 8 dims,
-  // the 16 lanes of a row group reading one 128-byte row together
+  // staging roles: K = 16-byte chunks (D/16 per row); V = 4 keys x 8 dims, the
+  // 16 lanes of a row group reading one 128-byte row together. Loads go through
+  // buffer descriptors whose size ends at this workgroup's last key, so rows
+  // past the range read as zeros without touching memory; the per-thread offset
+  // is fixed and the tile start is the scalar offset.
   constexpr int KPASS = (BK * D / 16) / 256;
+  constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor, gfx9 family
   const int v_dg = tid & 15, v_kq = tid >> 4;
   const bool v_role = v_dg < D / 8;
+  // the descriptors are wavefront-uniform; say so, or every load gets a
+  // readfirstlane loop around it
+  const int nrec = __builtin_amdgcn_readfirstlane(kend * D);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kplane), 0, nrec, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vplane), 0, nrec, kRsrcWord3);
+  int koff[KPASS];
+#pragma unroll
+  for (int p = 0; p < KPASS; ++p) {
+    const int c = tid + p * 256;
+    koff[p] = (c / (D / 16)) * D + 16 * (c % (D / 16));
+  }
+  const int voff = 4 * v_kq * D + 8 * v_dg;
   uint4 pk[KPASS];
   uint2 pv[4];
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      const int c = tid + p * 256, key = c / (D / 16), col = c % (D / 16);
-      pk[p] = uint4{0u, 0u, 0u, 0u};
-      if (kt + key < kend) pk[p] = *reinterpret_cast<const uint4 *>(kplane + static_cast<size_t>(kt + key) * D + 16 * col);
+      auto w = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[p], kt * D, 0);
+      pk[p] = uint4{w[0], w[1], w[2], w[3]};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = kt + 4 * v_kq + j;
-      pv[j] = uint2{0u, 0u};
-      if (v_role && key < kend) pv[j] = *reinterpret_cast<const uint2 *>(vplane + static_cast<size_t>(key) * D + 8 * v_dg);
+      auto w = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff + j * D, kt * D, 0);
+      pv[j] = uint2{w[0], w[1]};
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
       const int c = tid + p * 256, key = c / (D / 16), col = c % (D / 16);
-      *reinterpret_cast<uint4 *>(sK + key * KSTRIDE + 16 * col) = pk[p];
+      *reinterpret_cast<uint4 *>(sK[buf] + key * KSTRIDE + 16 * col) = pk[p];
     }
     if (v_role) {
       v2h vh[4][4];   // [key j][dim pair]
@@ -243,183 +306,148 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
         vh[j][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, false);
         vh[j][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, true);
       }
+      // keys 4kq..4kq+3: group kq/4, 16-byte slot 2(kq/4) + bit0(kq), half bit1(kq)
+      const int slot16 = 2 * (v_kq >> 2) + (v_kq & 1), half = (v_kq >> 1) & 1;
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
         const int row = 8 * v_dg + dd;
         v4h col = {vh[0][dd >> 1][dd & 1], vh[1][dd >> 1][dd & 1], vh[2][dd >> 1][dd & 1], vh[3][dd >> 1][dd & 1]};
-        *reinterpret_cast<v4h *>(sVt + row * VROW + 4 * (v_kq ^ vswz(row))) = col;
+        *reinterpret_cast<v4h *>(sVt[buf] + row * VROW + 8 * (slot16 ^ vswz(row)) + 4 * half) = col;
       }
     }
   };
 
-  // Scores come out of the QK MFMA already shifted by the column's reference
-  // max (the accumulator starts at -m_ref), in log2 units. P = exp2(s) is kept
-  // below 2^15; the reference is moved only when a tile would exceed that, or on
-  // the first tile, where it is set to the column max.
-  float m_ref[QB], l_run[QB];
-  v4f negm[QB];
-  v4f oacc[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_ref[qb] = 0.0f;
-    negm[qb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    l_run[qb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) oacc[qb][db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  int vbase[8];
+  // V^T fragment addressing: for row 32db + r, the 8 keys of PV step m for
+  // this lane sit in 16-byte slot 2m + hh, stored at (hh ^ r ^ (r >> 3)) ^
+  // 2((m ^ 2db) & 3): a per-lane base for each of the 4 values of (m ^ 2db) & 3
+  // plus an immediate row offset.
+  int vbase[4];
   {
-    const int m = (g ^ r ^ (r >> 3)) & 15;
+    const int mm = (hh ^ r ^ (r >> 3)) & 7;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) vbase[k] = r * VROW + 4 * (m ^ (2 * k));
+    for (int k = 0; k < 4; ++k) vbase[k] = r * VROW + 8 * (mm ^ (2 * k));
   }
 
-  if (kbeg < kend) load_tile(kbeg);
-  for (int kt = kbeg; kt < kend; kt += BK) {
-    __syncthreads();              // every wave is done reading the previous tile
-    store_tile();
+  // S^T for 32 keys (block kb of the tile in buffer buf) x this wave's 32
+  // queries, in log2 units. Register i holds key 8(i/4) + 4hh + (i%4).
+  auto score_block = [&](int buf, int kb, v16f &s) {
+    const uint8_t *krow = sK[buf] + (32 * kb + r) * KSTRIDE;
+#pragma unroll
+    for (int dh = 0; dh < DH; ++dh) {
+      const uint4 lo = *reinterpret_cast<const uint4 *>(krow + 64 * dh + 16 * hh);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(krow + 64 * dh + 32 + 16 * hh);
+      const v8i kf = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                      static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+      // term t's B-side scale is byte t of qscale[dh] (op_sel)
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qt[dh][0], dh == 0 ? v16f{} : s, 0, 0, 0, 127, 0, qscale[dh]);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qt[dh][1], s, 0, 0, 0, 127, 1, qscale[dh]);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qt[dh][2], s, 0, 0, 0, 127, 2, qscale[dh]);
+    }
+  };
+
+  // Online softmax against a reference max m_ref that moves only on the range's
+  // first block or when a score exceeds it by more than 2^15 (so P <= 2^15),
+  // then O^T += V^T P^T for the block's two PV steps of 16 keys. The row sum is
+  // taken over the fp16-rounded P (dot2 with ones into fp32), so rounding of a
+  // dominant weight cancels between numerator and denominator.
+  float m_ref = kNegBig, l_run = 0.0f;
+  v16f oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = v16f{};
+  auto softmax_pv = [&](v16f &s, int buf, int kt, int kb, bool forced) {
+    if (kt + BK > kend) {           // last, partial tile: keys past the range weigh 0
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kt + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= kend) s[i] = -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+    tmax = fmaxf(tmax, other_half(tmax));
+    const bool need = forced || tmax > m_ref + kShiftAt;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? tmax : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    const v2h ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    v8h pb[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      v2h h2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        h2[i] = v2h{static_cast<_Float16>(__builtin_amdgcn_exp2f(s[8 * half + 2 * i] - m_ref)),
+                    static_cast<_Float16>(__builtin_amdgcn_exp2f(s[8 * half + 2 * i + 1] - m_ref))};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run = __builtin_amdgcn_fdot2(h2[i], ones, l_run, false);
+      pb[half] = v8h{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
+    }
+    // k-slot 8hh + j <-> key 16m + 4hh + j and 8hh + 4 + j <-> key 16m + 8 +
+    // 4hh + j (j < 4), the same for A (V^T rows from LDS, one 16-byte read) and
+    // B (P^T from the score registers); register 8(m%2)+j of the block is key
+    // 16m + 8(j/4) + 4hh + (j%4).
+    const _Float16 *sVc = sVt[buf];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int m = 2 * kb + half;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const v8h va = *reinterpret_cast<const v8h *>(sVc + vbase[(m ^ (2 * db)) & 3] + 32 * db * VROW);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[half], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(kbeg);
+    store_tile(0);
+    if (ntiles > 1) load_tile(kbeg + BK);
     __syncthreads();
-    if (kt + BK < kend) load_tile(kt + BK);
-
-    // ---- S^T - m_ref = K Q^T - m_ref: 4 blocks of 16 keys x QB blocks -------
-    const bool partial = kt + BK > kend;
-    auto scores = [&](v4f (&s)[QB][4]) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint8_t *krow = sK + (16 * kb + r) * KSTRIDE;
-        uint4 lo = *reinterpret_cast<const uint4 *>(krow + 16 * g);
-        uint4 hi = {0u, 0u, 0u, 0u};
-        if (D == 128) hi = *reinterpret_cast<const uint4 *>(krow + 64 + 16 * g);
-        v8i kf = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                  static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          // the B-side scale of term t is byte t of qscale (op_sel)
-          v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qt[qb][0], negm[qb], 0, 0, 0, 127, 0, qscale[qb]);
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qt[qb][1], acc, 0, 0, 0, 127, 1, qscale[qb]);
-          s[qb][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qt[qb][2], acc, 0, 0, 0, 127, 2, qscale[qb]);
-        }
+    v16f s0, s1;
+    score_block(0, 0, s0);
+    for (int t = 0; t < ntiles; ++t) {
+      const int kt = kbeg + t * BK;
+      const int cur = t % 3;
+      score_block(cur, 1, s1);                     // next block's MFMAs first
+      softmax_pv(s0, cur, kt, 0, t == 0);
+      if (t + 1 < ntiles) {
+        store_tile((t + 1) % 3);                   // buffer last read two tiles ago
+        if (t + 2 < ntiles) load_tile(kt + 2 * BK);
       }
-      if (partial) {              // last, partial tile: keys past the range weigh 0
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (kt + 16 * kb + 4 * g + i >= kend) s[qb][kb][i] = -INFINITY;
-      }
-    };
-
-    // ---- P = exp2(s), fp16 for the PV MFMA --------------------------------------
-    v8h pb[QB][2];
-    float psum[QB];
-    auto exponentiate = [&](const v4f (&s)[4], int qb) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(s[2 * c][i]);
-          p[4 + i] = __builtin_amdgcn_exp2f(s[2 * c + 1][i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc += p[i];
-        pb[qb][c] = v8h{static_cast<_Float16>(p[0]), static_cast<_Float16>(p[1]), static_cast<_Float16>(p[2]),
-                        static_cast<_Float16>(p[3]), static_cast<_Float16>(p[4]), static_cast<_Float16>(p[5]),
-                        static_cast<_Float16>(p[6]), static_cast<_Float16>(p[7])};
-      }
-      psum[qb] = acc;
-    };
-    const bool first = kt == kbeg;
-    bool over = first;
-    {
-      v4f s[QB][4];
-      scores(s);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        exponentiate(s[qb], qb);
-        over = over || !(psum[qb] <= kPmax);   // also catches inf
-      }
-    }
-    if (__builtin_amdgcn_ballot_w64(over)) {
-      // Rare: recompute the scores (the K tile is still in LDS), move the
-      // reference of every column whose max exceeds it by 2^3 (all columns on
-      // the first tile), rescale what was accumulated and redo P.
-      v4f s[QB][4];
-      scores(s);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          tmax = fmaxf(tmax, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float shift = (first || tmax > 8.0f) ? tmax : 0.0f;
-        const float alpha = __builtin_amdgcn_exp2f(-shift);
-        m_ref[qb] += shift;
-        negm[qb] = v4f{-m_ref[qb], -m_ref[qb], -m_ref[qb], -m_ref[qb]};
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) oacc[qb][db] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s[qb][kb] -= shift;
-        exponentiate(s[qb], qb);
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += psum[qb];
-
-    // ---- O^T += V^T P^T: two chunks of 32 keys --------------------------------
-    // k-slot 8g+j <-> key 32c+4g+j and 8g+4+j <-> key 32c+16+4g+j (j < 4), the
-    // same for A (V^T from LDS) and B (P^T from the score registers).
-    // For row 16*db + r, the swizzled slot of logical slot 8c + 4o + g is
-    // (g ^ r ^ (r >> 3)) ^ 2*((4c) ^ (2o) ^ db): a per-lane base for each of
-    // the 8 values of (4c) ^ (2o) ^ db plus an immediate row offset.
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const _Float16 *v0p = sVt + vbase[(4 * c) ^ db] + 16 * db * VROW;
-        const _Float16 *v1p = sVt + vbase[(4 * c) ^ 2 ^ db] + 16 * db * VROW;
-        v4h v0 = *reinterpret_cast<const v4h *>(v0p);
-        v4h v1 = *reinterpret_cast<const v4h *>(v1p);
-        v8h va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qb][c], oacc[qb][db], 0, 0, 0);
-      }
+      __syncthreads();                             // publishes tile t+1
+      if (t + 1 < ntiles) score_block((t + 1) % 3, 0, s0);
+      softmax_pv(s1, cur, kt, 1, false);
     }
   }
 
   // ---- epilogue ---------------------------------------------------------------
+  // register i of d-block db holds dim 32db + 8(i/4) + 4hh + (i%4)
+  const float l_tot = l_run + other_half(l_run);
+  if (qi >= a.n_q) return;
+  if (a.splits == 1) {
+    const float f = a.scales[2 * H + h] / l_tot;
+    float *o = a.out + (static_cast<size_t>(qi) * H + h) * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const int qi = q0 + 16 * qb + r;
-    if (qi >= a.n_q) continue;
-    if (a.splits == 1) {
-      const float f = a.scales[2 * H + h] / l_tot;
-      float *o = a.out + (static_cast<size_t>(qi) * H + h) * D;
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        float4 v = {oacc[qb][db][0] * f, oacc[qb][db][1] * f, oacc[qb][db][2] * f, oacc[qb][db][3] * f};
-        *reinterpret_cast<float4 *>(o + 16 * db + 4 * g) = v;
+      for (int j = 0; j < 4; ++j) {
+        float4 v = {oacc[db][4 * j] * f, oacc[db][4 * j + 1] * f, oacc[db][4 * j + 2] * f, oacc[db][4 * j + 3] * f};
+        *reinterpret_cast<float4 *>(o + 32 * db + 8 * j + 4 * hh) = v;
       }
-    } else {
-      const size_t row = (static_cast<size_t>(split) * a.n_q + qi) * H + h;
-      float *o = a.part_o + row * D;
+  } else {
+    const size_t row = (static_cast<size_t>(split) * a.n_q + qi) * H + h;
+    float *o = a.part_o + row * D;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        float4 v = {oacc[qb][db][0], oacc[qb][db][1], oacc[qb][db][2], oacc[qb][db][3]};
-        *reinterpret_cast<float4 *>(o + 16 * db + 4 * g) = v;
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float4 v = {oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
+        *reinterpret_cast<float4 *>(o + 32 * db + 8 * j + 4 * hh) = v;
       }
-      if (g == 0) *reinterpret_cast<float2 *>(a.part_ml + 2 * row) = float2{m_ref[qb], l_tot};
-    }
+    if (hh == 0) *reinterpret_cast<float2 *>(a.part_ml + 2 * row) = float2{m_ref, l_tot};
   }
 }
 
@@ -464,9 +492,15 @@ int attend_splits(int n_q, int heads, int capacity) {
 hipError_t launch_attend(const AttendLaunch &a, hipStream_t st) {
   const int n_blocks = (a.n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock * a.heads * a.splits;
   const dim3 grid((n_blocks + 7) / 8 * 8);
-  constexpr int QB = kAttendQueriesPerBlock / 64;
-  if (a.head_dim == 128) hipLaunchKernelGGL((attend_kernel<128, QB>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attend_kernel<64, QB>), grid, dim3(256), 0, st, a);
+  const unsigned prep_threads = static_cast<unsigned>(a.n_q) * a.heads * (a.head_dim / 32);
+  const dim3 prep_grid((prep_threads + 255) / 256);
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL(query_prep_kernel<128>, prep_grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(query_prep_kernel<64>, prep_grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const size_t threads = static_cast<size_t>(a.n_q) * a.heads * (a.head_dim / 4);

@@ -252,23 +252,32 @@ static int n_valid_of(const sfkv_cache *c) {
   return static_cast<int>(c->tokens < c->cfg.capacity ? c->tokens : c->cfg.capacity);
 }
 
-// Partial results of split-KV attention: O rows [splits][n_q][heads][head_dim]
-// fp32, then (max, sum) pairs. The workspace is sized once per cache for its
-// largest write; a call with fewer queries caps its split count to fit, so one
-// buffer serves every token count.
-static size_t attend_rows_capacity(const sfkv_cache_cfg &cfg) {
-  const int s = sfkv::attend_splits(cfg.max_new_tokens, cfg.num_heads, cfg.capacity);
-  return s > 1 ? static_cast<size_t>(s) * cfg.max_new_tokens * cfg.num_heads : 0;
-}
+// Attend workspace, sized once per cache for its largest write (a call with
+// fewer queries caps its split count to fit, so one buffer serves every token
+// count):
+//   query terms   [max_new][heads][3][head_dim] bytes
+//   query scales  [max_new][heads][head_dim/32] words
+//   split partials: O rows [splits][n_q][heads][head_dim] fp32, then (max, sum)
+struct AttendWs {
+  size_t qterm, qscale, part_o, part_ml, total, rows_cap;
+};
 
-static size_t attend_ws_bytes(const sfkv_cache_cfg &cfg, size_t rows) {
-  if (rows == 0) return 0;
-  return align_up(rows * cfg.head_dim * sizeof(float), 256) + align_up(rows * 2 * sizeof(float), 256);
+static AttendWs attend_ws(const sfkv_cache_cfg &cfg) {
+  AttendWs w;
+  const size_t qh = static_cast<size_t>(cfg.max_new_tokens) * cfg.num_heads;
+  const int s = sfkv::attend_splits(cfg.max_new_tokens, cfg.num_heads, cfg.capacity);
+  w.rows_cap = s > 1 ? static_cast<size_t>(s) * qh : 0;
+  w.qterm = 0;
+  w.qscale = align_up(qh * 3 * cfg.head_dim, 256);
+  w.part_o = align_up(w.qscale + qh * (cfg.head_dim / 32) * sizeof(uint32_t), 256);
+  w.part_ml = align_up(w.part_o + w.rows_cap * cfg.head_dim * sizeof(float), 256);
+  w.total = align_up(w.part_ml + w.rows_cap * 2 * sizeof(float), 256);
+  return w;
 }
 
 size_t sfkv_attend_workspace_bytes(const sfkv_cache *c) {
   if (!c) return 0;
-  return attend_ws_bytes(c->cfg, attend_rows_capacity(c->cfg));
+  return attend_ws(c->cfg).total;
 }
 
 sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t n_q, float *out,
@@ -280,17 +289,14 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
   const int nv = n_valid_of(c);
-  const size_t rows_cap = attend_rows_capacity(c->cfg);
+  const AttendWs ws = attend_ws(c->cfg);
+  if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 256))
+    return fail(SFKV_EINVAL, "workspace missing, smaller than sfkv_attend_workspace_bytes() or not 256-byte aligned");
   const size_t rows_per_split = static_cast<size_t>(n_q) * c->cfg.num_heads;
   int splits = sfkv::attend_splits(n_q, c->cfg.num_heads, nv);
-  if (splits > 1 && static_cast<size_t>(splits) * rows_per_split > rows_cap)
-    splits = static_cast<int>(rows_cap / rows_per_split);
+  if (splits > 1 && static_cast<size_t>(splits) * rows_per_split > ws.rows_cap)
+    splits = static_cast<int>(ws.rows_cap / rows_per_split);
   if (splits < 2) splits = 1;
-  if (splits > 1) {
-    const size_t need = attend_ws_bytes(c->cfg, rows_cap);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-      return fail(SFKV_EINVAL, "workspace missing, smaller than sfkv_attend_workspace_bytes() or not 256-byte aligned");
-  }
   sfkv::AttendLaunch a;
   a.q = q;
   a.dtype = dtype;
@@ -306,13 +312,11 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   a.scales = reinterpret_cast<const float *>(c->base + c->scale_off);
   a.out = out;
   a.splits = splits;
-  a.part_o = nullptr;
-  a.part_ml = nullptr;
-  if (splits > 1) {
-    a.part_o = static_cast<float *>(workspace);
-    a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
-                                          align_up(rows_cap * c->cfg.head_dim * sizeof(float), 256));
-  }
+  uint8_t *wsb = static_cast<uint8_t *>(workspace);
+  a.qterm = wsb + ws.qterm;
+  a.qscale = reinterpret_cast<uint32_t *>(wsb + ws.qscale);
+  a.part_o = splits > 1 ? reinterpret_cast<float *>(wsb + ws.part_o) : nullptr;
+  a.part_ml = splits > 1 ? reinterpret_cast<float *>(wsb + ws.part_ml) : nullptr;
   return launched(sfkv::launch_attend(a, as_stream(stream)));
 }
 

@@ -49,6 +49,8 @@ struct AttendLaunch {
   int splits;                // key-range splits; 1 writes `out` directly
   float *part_o;             // [splits][n_q][heads][head_dim] when splits > 1
   float *part_ml;            // [splits][n_q][heads][2]
+  uint8_t *qterm;            // [n_q][heads][3][head_dim] E4M3 query terms
+  uint32_t *qscale;          // [n_q][heads][head_dim/32] E8M0 scales, byte t = term t
 };
 
 hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s);

@@ -219,9 +219,7 @@ class RingCache:
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         if workspace is None:
-            need = self.workspace_bytes()
-            if need:
-                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = torch.empty(self.workspace_bytes(), dtype=torch.uint8, device=q.device)
         attend(self.handle, q, out, workspace, stream)
         return out
 
