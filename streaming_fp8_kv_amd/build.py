@@ -29,7 +29,12 @@ COMMON = [
 # RoPE table with libm and must not use fast-math either.
 SOURCES = [
     ("cache_kernels.hip", ["-ffp-contract=off"]),
-    ("attend_kernel.hip", []),
+    # The attention loop issues the next block's score MFMAs before the current
+    # block's softmax so the two overlap; machine sinking would move those
+    # MFMAs down to their first use and serialise matrix and vector work.
+    # Inputs are finite by contract (masked scores are -inf, which stays
+    # allowed), so max needs no NaN canonicalisation and folds into v_max3.
+    ("attend_kernel.hip", ["-mllvm", "-disable-machine-sink=1", "-fno-honor-nans"]),
     ("sfkv_api.cpp", ["-x", "hip", "-ffp-contract=off", "-fno-fast-math"]),
 ]
 

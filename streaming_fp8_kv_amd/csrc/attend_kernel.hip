@@ -42,6 +42,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = kAttendKeysPerTile;      // 64 keys per LDS tile
 constexpr int KSTRIDE = 144;                // bytes per key row in LDS (128 + 16 pad)
@@ -291,29 +293,33 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
       pv[j] = uint2{w[0], w[1]};
     }
   };
-  auto store_tile = [&](int buf) {
+  // Staging of a loaded tile into LDS buffer buf, in three parts so that the
+  // pieces can sit between matrix instructions: K rows as they are, V widened
+  // to fp16 (exact) and stored transposed, one 8-byte column piece at a time.
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
       const int c = tid + p * 256, key = c / (D / 16), col = c % (D / 16);
       *reinterpret_cast<uint4 *>(sK[buf] + key * KSTRIDE + 16 * col) = pk[p];
     }
+  };
+  v2h vh[4][4];   // [key j][dim pair] of this thread's V piece
+  auto convert_v = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vh[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, false);
+      vh[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, true);
+      vh[j][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, false);
+      vh[j][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, true);
+    }
+  };
+  // keys 4kq..4kq+3: group kq/4, 16-byte slot 2(kq/4) + bit0(kq), half bit1(kq)
+  const int v_slot16 = 2 * (v_kq >> 2) + (v_kq & 1), v_half = (v_kq >> 1) & 1;
+  auto store_v = [&](int buf, int dd) {
     if (v_role) {
-      v2h vh[4][4];   // [key j][dim pair]
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vh[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, false);
-        vh[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, true);
-        vh[j][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, false);
-        vh[j][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, true);
-      }
-      // keys 4kq..4kq+3: group kq/4, 16-byte slot 2(kq/4) + bit0(kq), half bit1(kq)
-      const int slot16 = 2 * (v_kq >> 2) + (v_kq & 1), half = (v_kq >> 1) & 1;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int row = 8 * v_dg + dd;
-        v4h col = {vh[0][dd >> 1][dd & 1], vh[1][dd >> 1][dd & 1], vh[2][dd >> 1][dd & 1], vh[3][dd >> 1][dd & 1]};
-        *reinterpret_cast<v4h *>(sVt[buf] + row * VROW + 8 * (slot16 ^ vswz(row)) + 4 * half) = col;
-      }
+      const int row = 8 * v_dg + dd;
+      v4h col = {vh[0][dd >> 1][dd & 1], vh[1][dd >> 1][dd & 1], vh[2][dd >> 1][dd & 1], vh[3][dd >> 1][dd & 1]};
+      *reinterpret_cast<v4h *>(sVt[buf] + row * VROW + 8 * (v_slot16 ^ vswz(row)) + 4 * v_half) = col;
     }
   };
 
@@ -327,35 +333,50 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) vbase[k] = r * VROW + 8 * (mm ^ (2 * k));
   }
+  auto read_v = [&](int buf, int m, int db) {
+    return *reinterpret_cast<const v8h *>(sVt[buf] + vbase[(m ^ (2 * db)) & 3] + 32 * db * VROW);
+  };
 
-  // S^T for 32 keys (block kb of the tile in buffer buf) x this wave's 32
-  // queries, in log2 units. Register i holds key 8(i/4) + 4hh + (i%4).
-  auto score_block = [&](int buf, int kb, v16f &s) {
+  // K fragments of block kb (32 keys) of buffer buf: the A operand of the score
+  // MFMAs, one 32-byte fragment per 64-dim half.
+  auto read_k = [&](int buf, int kb, v8i kf[DH]) {
     const uint8_t *krow = sK[buf] + (32 * kb + r) * KSTRIDE;
 #pragma unroll
     for (int dh = 0; dh < DH; ++dh) {
       const uint4 lo = *reinterpret_cast<const uint4 *>(krow + 64 * dh + 16 * hh);
       const uint4 hi = *reinterpret_cast<const uint4 *>(krow + 64 * dh + 32 + 16 * hh);
-      const v8i kf = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                      static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-      // term t's B-side scale is byte t of qscale[dh] (op_sel)
-      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qt[dh][0], dh == 0 ? v16f{} : s, 0, 0, 0, 127, 0, qscale[dh]);
-      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qt[dh][1], s, 0, 0, 0, 127, 1, qscale[dh]);
-      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qt[dh][2], s, 0, 0, 0, 127, 2, qscale[dh]);
+      kf[dh] = v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                   static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    }
+  };
+  // Score MFMA i of a block (dim half i / 3, query term i % 3): S^T for the
+  // block's 32 keys x this wave's 32 queries, in log2 units; register i of s
+  // holds key 8(i/4) + 4hh + (i%4). Term t's B-side scale is byte t of
+  // qscale[dh] (op_sel).
+  auto qk_step = [&](const v8i kf[DH], int i, v16f &s) {
+    const int dh = i / 3;
+    switch (i % 3) {
+      case 0: s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[dh], qt[dh][0], i == 0 ? v16f{} : s, 0, 0, 0, 127, 0, qscale[dh]); break;
+      case 1: s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[dh], qt[dh][1], s, 0, 0, 0, 127, 1, qscale[dh]); break;
+      default: s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[dh], qt[dh][2], s, 0, 0, 0, 127, 2, qscale[dh]); break;
     }
   };
 
   // Online softmax against a reference max m_ref that moves only on the range's
-  // first block or when a score exceeds it by more than 2^15 (so P <= 2^15),
-  // then O^T += V^T P^T for the block's two PV steps of 16 keys. The row sum is
-  // taken over the fp16-rounded P (dot2 with ones into fp32), so rounding of a
+  // first block or when a score exceeds it by more than 2^15 (so P <= 2^15,
+  // inside fp16). P = exp2(s - m_ref) is rounded to fp16 and the row sum is
+  // taken over the rounded values (dot2 with ones into fp32), so rounding of a
   // dominant weight cancels between numerator and denominator.
   float m_ref = kNegBig, l_run = 0.0f;
   v16f oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = v16f{};
-  auto softmax_pv = [&](v16f &s, int buf, int kt, int kb, bool forced) {
-    if (kt + BK > kend) {           // last, partial tile: keys past the range weigh 0
+  const v2h ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+
+  // Head of a block: mask keys past the range (last tile only), block max,
+  // and the rare rescale of the running output.
+  auto block_head = [&](v16f &s, int kt, int kb, bool forced) {
+    if (kt + BK > kend) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (kt + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= kend) s[i] = -INFINITY;
@@ -372,54 +393,111 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
-    const v2h ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    v8h pb[2];
+  };
+  // Four weights of a block as two packed fp16 pairs, added to the row sum.
+  auto exp4 = [&](const v16f &s, int i0, uint32_t *w) {
+    const v2h a = __builtin_convertvector(
+        (float2_t){__builtin_amdgcn_exp2f(s[i0] - m_ref), __builtin_amdgcn_exp2f(s[i0 + 1] - m_ref)}, v2h);
+    const v2h b = __builtin_convertvector(
+        (float2_t){__builtin_amdgcn_exp2f(s[i0 + 2] - m_ref), __builtin_amdgcn_exp2f(s[i0 + 3] - m_ref)}, v2h);
+    l_run = __builtin_amdgcn_fdot2(a, ones, l_run, false);
+    l_run = __builtin_amdgcn_fdot2(b, ones, l_run, false);
+    w[0] = __builtin_bit_cast(uint32_t, a);
+    w[1] = __builtin_bit_cast(uint32_t, b);
+  };
+
+  // One region per block, written in issue order with scheduling fences so that
+  // the matrix core always has work queued while the vector ALU runs: the next
+  // block's score MFMAs are interleaved with this block's exponentials, then
+  // this block's PV MFMAs with the LDS staging of the next tile. In PV, k-slot
+  // 8hh + j <-> key 16m + 4hh + j and 8hh + 4 + j <-> key 16m + 8 + 4hh + j
+  // (j < 4), the same for A (V^T rows from LDS, one 16-byte read) and B (P^T
+  // from the score registers); register 8(m%2)+j of the block is key 16m +
+  // 8(j/4) + 4hh + (j%4).
+  constexpr int NQK = 3 * DH;           // score MFMAs per block
+  constexpr int NDB = D / 32;           // PV MFMAs per 16 keys
+  auto region = [&](const v16f &s_cur, v16f &s_next, int qbuf, int qkb, int vbuf, int kb, bool stage, int sbuf) {
+    v8i kf[DH];
+    read_k(qbuf, qkb, kf);
+    v8h va[NDB];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      v2h h2[4];
+    for (int db = 0; db < NDB; ++db) va[db] = read_v(vbuf, 2 * kb, db);
+    uint32_t pw[8];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        h2[i] = v2h{static_cast<_Float16>(__builtin_amdgcn_exp2f(s[8 * half + 2 * i] - m_ref)),
-                    static_cast<_Float16>(__builtin_amdgcn_exp2f(s[8 * half + 2 * i + 1] - m_ref))};
+    for (int i = 0; i < NQK; ++i) {
+      qk_step(kf, i, s_next);
+      if (i < 4) exp4(s_cur, 4 * i, pw + 2 * i);
+      if (i == NQK - 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l_run = __builtin_amdgcn_fdot2(h2[i], ones, l_run, false);
-      pb[half] = v8h{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
-    }
-    // k-slot 8hh + j <-> key 16m + 4hh + j and 8hh + 4 + j <-> key 16m + 8 +
-    // 4hh + j (j < 4), the same for A (V^T rows from LDS, one 16-byte read) and
-    // B (P^T from the score registers); register 8(m%2)+j of the block is key
-    // 16m + 8(j/4) + 4hh + (j%4).
-    const _Float16 *sVc = sVt[buf];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int m = 2 * kb + half;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const v8h va = *reinterpret_cast<const v8h *>(sVc + vbase[(m ^ (2 * db)) & 3] + 32 * db * VROW);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[half], oacc[db], 0, 0, 0);
+        for (int g = NQK; g < 4; ++g) exp4(s_cur, 4 * g, pw + 2 * g);
+        if (stage) { store_k(sbuf); convert_v(); }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const v8h pb0 = __builtin_bit_cast(v8h, (v4u_t){pw[0], pw[1], pw[2], pw[3]});
+    const v8h pb1 = __builtin_bit_cast(v8h, (v4u_t){pw[4], pw[5], pw[6], pw[7]});
+    v8h vb[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vb[db] = read_v(vbuf, 2 * kb + 1, db);
+    constexpr int SPER = 8 / (2 * NDB);   // V column stores per PV MFMA
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db], pb0, oacc[db], 0, 0, 0);
+      if (stage) {
+#pragma unroll
+        for (int k = 0; k < SPER; ++k) store_v(sbuf, db * SPER + k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db], pb1, oacc[db], 0, 0, 0);
+      if (stage) {
+#pragma unroll
+        for (int k = 0; k < SPER; ++k) store_v(sbuf, (NDB + db) * SPER + k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   if (ntiles > 0) {
+    // Prologue: tile 0 in buffer 0, tile 1 in registers, scores of block 0.
     load_tile(kbeg);
-    store_tile(0);
-    if (ntiles > 1) load_tile(kbeg + BK);
+    store_k(0);
+    convert_v();
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) store_v(0, dd);
+    load_tile(kbeg + BK);                          // past the range reads zeros
     __syncthreads();
     v16f s0, s1;
-    score_block(0, 0, s0);
-    for (int t = 0; t < ntiles; ++t) {
+    {
+      v8i kf[DH];
+      read_k(0, 0, kf);
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) qk_step(kf, i, s0);
+    }
+    // Tile t sits in buffer t % 3. Block 2t's region scores block 2t+1 and
+    // stages tile t+1 (loaded one region earlier) into buffer (t+1) % 3, last
+    // read before the previous barrier; after the barrier, block 2t+1's region
+    // scores block 2t+2 from that buffer and loads tile t+2 into registers.
+    // The last tile's region scores and stages a tile past the range; that work
+    // is discarded (loads past the range read zeros), which keeps every region
+    // free of branches.
+    // Unrolled by three so that every LDS buffer offset is an immediate.
+    auto tile_step = [&](int t, int cur, int nxt) {
       const int kt = kbeg + t * BK;
-      const int cur = t % 3;
-      score_block(cur, 1, s1);                     // next block's MFMAs first
-      softmax_pv(s0, cur, kt, 0, t == 0);
-      if (t + 1 < ntiles) {
-        store_tile((t + 1) % 3);                   // buffer last read two tiles ago
-        if (t + 2 < ntiles) load_tile(kt + 2 * BK);
-      }
+      block_head(s0, kt, 0, t == 0);
+      region(s0, s1, cur, 1, cur, 0, true, nxt);
+      block_head(s1, kt, 1, false);
       __syncthreads();                             // publishes tile t+1
-      if (t + 1 < ntiles) score_block((t + 1) % 3, 0, s0);
-      softmax_pv(s1, cur, kt, 1, false);
+      load_tile(kt + 2 * BK);
+      region(s1, s0, nxt, 0, cur, 1, false, 0);
+    };
+    for (int t = 0; t < ntiles; t += 3) {
+      tile_step(t, 0, 1);
+      if (t + 1 < ntiles) tile_step(t + 1, 1, 2);
+      if (t + 2 < ntiles) tile_step(t + 2, 2, 0);
     }
   }
 
