@@ -61,24 +61,6 @@ constexpr float kNegBig = -1.0e30f;
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// 16 consecutive query elements as fp32.
-__device__ inline void load16(const void *q, size_t elem, int dtype, float *x) {
-  if (dtype == 0) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + elem);
-    uint4 a = p[0], b = p[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { x[2 * j] = bf16_lo(w[j]); x[2 * j + 1] = bf16_hi(w[j]); }
-  } else {
-    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + elem);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float4 v = p[j];
-      x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
-    }
-  }
-}
-
 // Smallest e with m * 2^-e <= 448, from the exact binary exponent of m
 // (448 = 0.875 * 2^9); clamped to the E8M0 range.
 __device__ inline int block_exponent(float m) {
@@ -89,52 +71,59 @@ __device__ inline int block_exponent(float m) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Encode 16 values (already divided by the block scale) into 4 words.
-__device__ inline void encode16(const float *x, int *w) {
+// 8 consecutive query elements as fp32.
+__device__ inline void load8(const void *q, size_t elem, int dtype, float *x) {
+  if (dtype == 0) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + elem);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int t = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * j], x[4 * j + 1], 0, false);
-    w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * j + 2], x[4 * j + 3], t, true);
+    for (int j = 0; j < 4; ++j) { x[2 * j] = bf16_lo(u[j]); x[2 * j + 1] = bf16_hi(u[j]); }
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + elem);
+    const float4 v0 = p[0], v1 = p[1];
+    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
   }
 }
 
-__device__ inline void decode16(const int *w, float *x) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);
-    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);
-    x[4 * j] = lo[0]; x[4 * j + 1] = lo[1]; x[4 * j + 2] = hi[0]; x[4 * j + 3] = hi[1];
-  }
+// Max over the four lanes of an aligned lane quad (DPP quad permutations).
+__device__ inline float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));  // [1,0,3,2]
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));  // [2,3,0,1]
+  return v;
 }
 
-// Query preparation, one thread per (query, head, 32-dim block): RoPE at the
-// query's position, the factor scale_k * log2(e) / sqrt(d) folded in, then three
-// E4M3 terms, each the rounding of what the previous terms left over, with one
-// power-of-two (E8M0) scale per term for the block. Codes are stored in natural
-// dim order, [query][head][term][dim]; the scale bytes of terms 0..2 are packed
-// into one word per block. A 32-dim block is exactly one scale block of the
-// 32x32x64 block-scaled MFMA.
+// Query preparation, once per call: RoPE at the query's position, the factor
+// scale_k * log2(e) / sqrt(d) folded in, then three E4M3 terms, each the
+// rounding of what the earlier terms left over, each with one power-of-two
+// (E8M0) scale per 32-dim block (exactly one scale block of the 32x32x64
+// block-scaled MFMA). A three-term query carries about 12 significant bits.
+// One thread per 8 dims; the four threads of a block sit in one lane quad and
+// share the block maximum through DPP. Codes are stored in natural dim order,
+// [query][head][term][dim]; the scale bytes of terms 0..2 are packed into one
+// word per block.
 template <int D>
 __global__ __launch_bounds__(256) void query_prep_kernel(AttendLaunch a) {
-  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
   constexpr int NB = D / 32;
-  if (idx >= static_cast<unsigned>(a.n_q) * a.heads * NB) return;
-  const int b = idx % NB;
-  const unsigned qh = idx / NB;                 // qi * heads + h
+  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
+  // the element count is a multiple of 4, so a lane quad is all in or all out
+  if (idx >= static_cast<unsigned>(a.n_q) * a.heads * (D / 8)) return;
+  const int g = idx & 3;                        // 8-dim group inside the block
+  const unsigned blk = idx >> 2;
+  const int b = blk % NB;
+  const unsigned qh = blk / NB;                 // qi * heads + h
   const int h = qh % a.heads;
   const int qi = qh / a.heads;
-  float x[32];
-  const size_t base = static_cast<size_t>(qh) * D + 32 * b;
-  load16(a.q, base, a.dtype, x);
-  load16(a.q, base + 16, a.dtype, x + 16);
+  float x[8];
+  load8(a.q, static_cast<size_t>(qh) * D + 32 * b + 8 * g, a.dtype, x);
   // A rebase can leave the last write's queries at negative positions;
   // cos(-x) = cos(x) and sin(-x) = -sin(x) reuse the row of |p|.
   const int qp = a.qpos0 + qi;
   const float sgn = qp < 0 ? -1.0f : 1.0f;
-  const RopePair *row = a.rope + static_cast<size_t>(qp < 0 ? -qp : qp) * (D / 2) + 16 * b;
+  const RopePair *row = a.rope + static_cast<size_t>(qp < 0 ? -qp : qp) * (D / 2) + 16 * b + 4 * g;
   const float qs = a.scales[h] * kLog2e * (1.0f / sqrtf(static_cast<float>(D)));
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 4; ++j) {
     RopePair cs = row[j];
     cs.s *= sgn;
     const float u = x[2 * j], v = x[2 * j + 1];
@@ -146,25 +135,28 @@ __global__ __launch_bounds__(256) void query_prep_kernel(AttendLaunch a) {
   for (int t = 0; t < 3; ++t) {
     float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) m = fmaxf(m, fabsf(x[j]));
-    const int e = block_exponent(m);
-    float y[32];
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+    const int e = block_exponent(quad_max(m));
+    int w[2];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) y[j] = ldexpf(x[j], -e);
-    int w[8];
-    encode16(y, w);
-    encode16(y + 16, w + 4);
-    float dq[32];
-    decode16(w, dq);
-    decode16(w + 4, dq + 16);
+    for (int j = 0; j < 2; ++j) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j], -e), ldexpf(x[4 * j + 1], -e), 0, false);
+      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j + 2], -e), ldexpf(x[4 * j + 3], -e), lo, true);
+    }
 #pragma unroll
-    for (int j = 0; j < 32; ++j) x[j] -= ldexpf(dq[j], e);
-    uint4 *dst = reinterpret_cast<uint4 *>(a.qterm + (static_cast<size_t>(qh) * 3 + t) * D + 32 * b);
-    dst[0] = uint4{static_cast<uint32_t>(w[0]), static_cast<uint32_t>(w[1]), static_cast<uint32_t>(w[2]), static_cast<uint32_t>(w[3])};
-    dst[1] = uint4{static_cast<uint32_t>(w[4]), static_cast<uint32_t>(w[5]), static_cast<uint32_t>(w[6]), static_cast<uint32_t>(w[7])};
+    for (int j = 0; j < 2; ++j) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);
+      x[4 * j] -= ldexpf(lo[0], e);
+      x[4 * j + 1] -= ldexpf(lo[1], e);
+      x[4 * j + 2] -= ldexpf(hi[0], e);
+      x[4 * j + 3] -= ldexpf(hi[1], e);
+    }
+    *reinterpret_cast<uint2 *>(a.qterm + (static_cast<size_t>(qh) * 3 + t) * D + 32 * b + 8 * g) =
+        uint2{static_cast<uint32_t>(w[0]), static_cast<uint32_t>(w[1])};
     packed |= static_cast<uint32_t>(127 + e) << (8 * t);
   }
-  a.qscale[static_cast<size_t>(qh) * NB + b] = packed;
+  if (g == 0) a.qscale[static_cast<size_t>(qh) * NB + b] = packed;
 }
 
 // Q terms of one lane of a 32-query block (column r = lane & 31, half
@@ -373,17 +365,21 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   for (int db = 0; db < D / 32; ++db) oacc[db] = v16f{};
   const v2h ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
-  // Head of a block: mask keys past the range (last tile only), block max,
-  // and the rare rescale of the running output.
-  auto block_head = [&](v16f &s, int kt, int kb, bool forced) {
+  // Maximum of a block's 32 scores per query column (both wave halves).
+  auto block_max = [&](const v16f &s) {
+    float t = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    t = fmaxf(t, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+    return fmaxf(t, other_half(t));
+  };
+  // Head of a block: mask keys past the range (last tile only, which also
+  // recomputes the block max), then the rare rescale of the running output.
+  auto block_head = [&](v16f &s, float tmax, int kt, int kb, bool forced) {
     if (kt + BK > kend) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (kt + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= kend) s[i] = -INFINITY;
+      tmax = block_max(s);
     }
-    float tmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-    tmax = fmaxf(tmax, other_half(tmax));
     const bool need = forced || tmax > m_ref + kShiftAt;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float m_new = need ? tmax : m_ref;
@@ -416,7 +412,8 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   // 8(j/4) + 4hh + (j%4).
   constexpr int NQK = 3 * DH;           // score MFMAs per block
   constexpr int NDB = D / 32;           // PV MFMAs per 16 keys
-  auto region = [&](const v16f &s_cur, v16f &s_next, int qbuf, int qkb, int vbuf, int kb, bool stage, int sbuf) {
+  auto region = [&](const v16f &s_cur, v16f &s_next, float &tmax_next, int qbuf, int qkb, int vbuf, int kb,
+                    bool stage, int sbuf, bool load, int kt_load) {
     v8i kf[DH];
     read_k(qbuf, qkb, kf);
     v8h va[NDB];
@@ -427,6 +424,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       qk_step(kf, i, s_next);
+      if (load && i == 0) load_tile(kt_load);
       if (i < 4) exp4(s_cur, 4 * i, pw + 2 * i);
       if (i == NQK - 1) {
 #pragma unroll
@@ -457,6 +455,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 #pragma unroll
         for (int k = 0; k < SPER; ++k) store_v(sbuf, (NDB + db) * SPER + k);
       }
+      if (db == NDB - 1) tmax_next = block_max(s_next);   // in the shadow of the PV MFMAs
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -471,11 +470,13 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
     load_tile(kbeg + BK);                          // past the range reads zeros
     __syncthreads();
     v16f s0, s1;
+    float t0, t1;
     {
       v8i kf[DH];
       read_k(0, 0, kf);
 #pragma unroll
       for (int i = 0; i < NQK; ++i) qk_step(kf, i, s0);
+      t0 = block_max(s0);
     }
     // Tile t sits in buffer t % 3. Block 2t's region scores block 2t+1 and
     // stages tile t+1 (loaded one region earlier) into buffer (t+1) % 3, last
@@ -487,12 +488,11 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
     // Unrolled by three so that every LDS buffer offset is an immediate.
     auto tile_step = [&](int t, int cur, int nxt) {
       const int kt = kbeg + t * BK;
-      block_head(s0, kt, 0, t == 0);
-      region(s0, s1, cur, 1, cur, 0, true, nxt);
-      block_head(s1, kt, 1, false);
+      block_head(s0, t0, kt, 0, t == 0);
+      region(s0, s1, t1, cur, 1, cur, 0, true, nxt, false, 0);
+      block_head(s1, t1, kt, 1, false);
       __syncthreads();                             // publishes tile t+1
-      load_tile(kt + 2 * BK);
-      region(s1, s0, nxt, 0, cur, 1, false, 0);
+      region(s1, s0, t0, nxt, 0, cur, 1, false, 0, true, kt + 2 * BK);
     };
     for (int t = 0; t < ntiles; t += 3) {
       tile_step(t, 0, 1);
@@ -529,28 +529,53 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   }
 }
 
-// Merge split partials: one thread per 4 output dims of one (query, head).
-template <int D>
+// Merge split partials: one thread per 8 output dims of one (query, head) row.
+// NS > 0 fixes the split count at compile time so every load is issued at once.
+template <int D, int NS>
 __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t rows = static_cast<size_t>(a.n_q) * a.heads;
-  if (idx >= rows * (D / 4)) return;
-  const size_t row = idx / (D / 4);
-  const int c4 = static_cast<int>(idx % (D / 4));
+  if (idx >= rows * (D / 8)) return;
+  const size_t row = idx / (D / 8);
+  const int c8 = static_cast<int>(idx % (D / 8));
   const int h = static_cast<int>(row % a.heads);
+  const int ns = NS > 0 ? NS : a.splits;
   float mstar = kNegBig;
-  for (int sp = 0; sp < a.splits; ++sp) mstar = fmaxf(mstar, a.part_ml[2 * (sp * rows + row)]);
+#pragma unroll
+  for (int sp = 0; sp < (NS > 0 ? NS : 16); ++sp) {
+    if (NS == 0 && sp >= ns) break;
+    mstar = fmaxf(mstar, a.part_ml[2 * (sp * rows + row)]);
+  }
   float L = 0.0f;
-  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int sp = 0; sp < a.splits; ++sp) {
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int sp = 0; sp < (NS > 0 ? NS : 16); ++sp) {
+    if (NS == 0 && sp >= ns) break;
     const size_t prow = sp * rows + row;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * prow] - mstar);
-    L += w * a.part_ml[2 * prow + 1];
-    const float4 o = *reinterpret_cast<const float4 *>(a.part_o + prow * D + 4 * c4);
-    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+    const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * prow);
+    const float w = __builtin_amdgcn_exp2f(ml.x - mstar);
+    L += w * ml.y;
+    const float4 *o = reinterpret_cast<const float4 *>(a.part_o + prow * D + 8 * c8);
+    const float4 o0 = o[0], o1 = o[1];
+    acc[0] += w * o0.x; acc[1] += w * o0.y; acc[2] += w * o0.z; acc[3] += w * o0.w;
+    acc[4] += w * o1.x; acc[5] += w * o1.y; acc[6] += w * o1.z; acc[7] += w * o1.w;
   }
   const float f = a.scales[2 * a.heads + h] / L;
-  *reinterpret_cast<float4 *>(a.out + row * D + 4 * c4) = float4{acc.x * f, acc.y * f, acc.z * f, acc.w * f};
+  float4 *dst = reinterpret_cast<float4 *>(a.out + row * D + 8 * c8);
+  dst[0] = float4{acc[0] * f, acc[1] * f, acc[2] * f, acc[3] * f};
+  dst[1] = float4{acc[4] * f, acc[5] * f, acc[6] * f, acc[7] * f};
+}
+
+template <int D>
+void launch_combine(const AttendLaunch &a, hipStream_t st) {
+  const size_t threads = static_cast<size_t>(a.n_q) * a.heads * (D / 8);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  switch (a.splits) {
+    case 2: hipLaunchKernelGGL((combine_kernel<D, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((combine_kernel<D, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((combine_kernel<D, 0>), grid, dim3(256), 0, st, a); break;
+  }
 }
 
 }  // namespace
@@ -570,21 +595,17 @@ int attend_splits(int n_q, int heads, int capacity) {
 hipError_t launch_attend(const AttendLaunch &a, hipStream_t st) {
   const int n_blocks = (a.n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock * a.heads * a.splits;
   const dim3 grid((n_blocks + 7) / 8 * 8);
-  const unsigned prep_threads = static_cast<unsigned>(a.n_q) * a.heads * (a.head_dim / 32);
+  const unsigned prep_threads = static_cast<unsigned>(a.n_q) * a.heads * (a.head_dim / 8);
   const dim3 prep_grid((prep_threads + 255) / 256);
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(query_prep_kernel<128>, prep_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(256), 0, st, a);
+    if (a.splits > 1) launch_combine<128>(a, st);
   } else {
     hipLaunchKernelGGL(query_prep_kernel<64>, prep_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(256), 0, st, a);
+    if (a.splits > 1) launch_combine<64>(a, st);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
-  const size_t threads = static_cast<size_t>(a.n_q) * a.heads * (a.head_dim / 4);
-  const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
-  if (a.head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(combine_kernel<64>, dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

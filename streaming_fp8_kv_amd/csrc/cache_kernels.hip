@@ -79,6 +79,7 @@ __device__ inline float scaled(float x, float inv) {
 // in, 16 B of K codes and 16 B of V codes out. Consecutive threads walk the
 // dims of a head, then the heads of a token, so the reads are fully coalesced
 // and each 128-byte row of a code plane is written by 8 adjacent lanes.
+template <int DT>   // input dtype, 0 bf16, 1 fp32: straight-line loads
 __global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
   // 32-bit indexing: the host keeps every code plane below 2^31 bytes.
   const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 4;
@@ -99,30 +100,31 @@ __global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
   const float inv_k = a.scales[a.heads + h];
   const float inv_v = a.scales[3 * a.heads + h];
 
-  float x[16];
-  load8(a.k, in_elem, a.dtype, x);
-  load8(a.k, in_elem + 8, a.dtype, x + 8);
+  // every load is issued before the first store: K, V and the table row
+  float x[16], y[16];
+  load8(a.k, in_elem, DT, x);
+  load8(a.k, in_elem + 8, DT, x + 8);
+  load8(a.v, in_elem, DT, y);
+  load8(a.v, in_elem + 8, DT, y + 8);
   const float4 *row = reinterpret_cast<const float4 *>(a.rope + static_cast<size_t>(p) * (a.head_dim >> 1) + c * 8);
+  float4 cs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cs[j] = row[j];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float4 cs = row[j];
-    rotate_pair(x[4 * j], x[4 * j + 1], RopePair{cs.x, cs.y});
-    rotate_pair(x[4 * j + 2], x[4 * j + 3], RopePair{cs.z, cs.w});
+    rotate_pair(x[4 * j], x[4 * j + 1], RopePair{cs[j].x, cs[j].y});
+    rotate_pair(x[4 * j + 2], x[4 * j + 3], RopePair{cs[j].z, cs[j].w});
   }
-  uint4 kw;
+  uint4 kw, vw;
   kw.x = encode4(scaled(x[0], inv_k), scaled(x[1], inv_k), scaled(x[2], inv_k), scaled(x[3], inv_k));
   kw.y = encode4(scaled(x[4], inv_k), scaled(x[5], inv_k), scaled(x[6], inv_k), scaled(x[7], inv_k));
   kw.z = encode4(scaled(x[8], inv_k), scaled(x[9], inv_k), scaled(x[10], inv_k), scaled(x[11], inv_k));
   kw.w = encode4(scaled(x[12], inv_k), scaled(x[13], inv_k), scaled(x[14], inv_k), scaled(x[15], inv_k));
+  vw.x = encode4(scaled(y[0], inv_v), scaled(y[1], inv_v), scaled(y[2], inv_v), scaled(y[3], inv_v));
+  vw.y = encode4(scaled(y[4], inv_v), scaled(y[5], inv_v), scaled(y[6], inv_v), scaled(y[7], inv_v));
+  vw.z = encode4(scaled(y[8], inv_v), scaled(y[9], inv_v), scaled(y[10], inv_v), scaled(y[11], inv_v));
+  vw.w = encode4(scaled(y[12], inv_v), scaled(y[13], inv_v), scaled(y[14], inv_v), scaled(y[15], inv_v));
   *reinterpret_cast<uint4 *>(a.k8 + out_off) = kw;
-
-  load8(a.v, in_elem, a.dtype, x);
-  load8(a.v, in_elem + 8, a.dtype, x + 8);
-  uint4 vw;
-  vw.x = encode4(scaled(x[0], inv_v), scaled(x[1], inv_v), scaled(x[2], inv_v), scaled(x[3], inv_v));
-  vw.y = encode4(scaled(x[4], inv_v), scaled(x[5], inv_v), scaled(x[6], inv_v), scaled(x[7], inv_v));
-  vw.z = encode4(scaled(x[8], inv_v), scaled(x[9], inv_v), scaled(x[10], inv_v), scaled(x[11], inv_v));
-  vw.w = encode4(scaled(x[12], inv_v), scaled(x[13], inv_v), scaled(x[14], inv_v), scaled(x[15], inv_v));
   *reinterpret_cast<uint4 *>(a.v8 + out_off) = vw;
 
   if (h == 0 && c == 0) a.pos[slot] = p;
@@ -214,7 +216,8 @@ inline unsigned blocks_for(size_t threads, unsigned per_block) {
 
 hipError_t launch_write(const WriteLaunch &a, hipStream_t s) {
   const size_t threads = static_cast<size_t>(a.n) * a.heads * (a.head_dim >> 4);
-  hipLaunchKernelGGL(write_kernel, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
+  if (a.dtype == 0) hipLaunchKernelGGL(write_kernel<0>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(write_kernel<1>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
