@@ -11,10 +11,12 @@ resident before the timed region starts.
 Prints one JSON line. ``value`` is microseconds per cache_write + attend call
 (step time / 240). ``roofline`` is for attend, the dominant call: algorithmic
 FLOPs per call (4 * n * slots * heads * head_dim) over its average duration
-from HIP events recorded around every attend call inside the timed region, on
-the stream the kernels run on, against the dense FP8 MFMA peak. One attend call
+from HIP events recorded around every attend call of the first and the last
+timed step, on the stream the kernels run on, against the dense FP8 MFMA
+peak. One attend call
 is up to three kernel launches (query prep, attention, split combine); the
-rocprofv3 summary lists each. cache_write alone and the position reset (one
+rocprofv3 summary lists each. cache_write alone, the same
+step captured once as a HIP graph and replayed, and the position reset (one
 delta rotation per cache) are timed in separate regions after the timed one and
 reported under ``extra``. ``cpu_baseline`` times the CPU oracle on a bounded
 sample.
@@ -103,7 +105,7 @@ def main():
     sw = Sweep(sfkv, n_caches=n_calls, spec=spec)
     sw.prefill()
     torch.cuda.synchronize()
-    if sw.positions_left() < args.warmup + args.steps + 2:
+    if sw.positions_left() < args.warmup + args.steps + 3:
         raise SystemExit("too many steps for the position range; lower --steps/--warmup")
 
     stream = torch.cuda.current_stream()
@@ -111,20 +113,26 @@ def main():
         sw.step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, events around every attend launch ----------
+    # ---- timed region: K steps; events around every attend call of the first
+    # and the last step (each event pair costs a few microseconds of stream
+    # time, so recording them on every step would inflate the step time) ----
     E = torch.cuda.Event
     ev_start, ev_end = E(enable_timing=True), E(enable_timing=True)
-    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps * n_calls)]
+    sampled = sorted({0, args.steps - 1})
+    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(len(sampled) * n_calls)]
     torch.cuda.synchronize()
     ev_start.record(stream)
     j = 0
-    for _ in range(args.steps):
+    for step in range(args.steps):
+        timed = step in sampled
         for c, (q, k, v), out in zip(sw.caches, sw.frames, sw.outs):
             sfkv.cache_write(c.handle, k, v, stream)
-            att[j][0].record(stream)
+            if timed:
+                att[j][0].record(stream)
             sfkv.attend(c.handle, q, out, sw.workspace, stream)
-            att[j][1].record(stream)
-            j += 1
+            if timed:
+                att[j][1].record(stream)
+                j += 1
     ev_end.record(stream)
     torch.cuda.synchronize()
     total_ms = ev_start.elapsed_time(ev_end)
@@ -140,6 +148,27 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     write_us = sum(a.elapsed_time(b) for a, b in wr) * 1e3 / len(wr)
+
+    # ---- the same step captured once as a HIP graph and replayed -----------
+    # (the capture enqueues one step's 480 launches; replays repeat it with the
+    # captured arguments, i.e. the same writes at the same positions)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            sw.step()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = E(enable_timing=True), E(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
 
     # ---- position reset: one delta rotation of every cache ------------------
     rb = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
@@ -184,6 +213,8 @@ def main():
             "rebase_us_per_cache": round(rebase_us, 3),
             "rebase_hbm_frac": round(rebase_bytes / (rebase_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "reset_step_extra_ms": round(rebase_us * n_calls / 1e3, 4),
+            "graph_ms_per_step": round(graph_ms, 4),
+            "graph_us_per_call": round(graph_ms * 1e3 / n_calls, 3),
         },
     }
     if not args.no_cpu_baseline:

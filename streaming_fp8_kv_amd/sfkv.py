@@ -175,11 +175,12 @@ class Rope:
         if n == 0:
             raise ValueError("invalid head_dim or max_position")
         self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self._destroy = _lib.sfkv_rope_destroy     # still reachable at interpreter exit
         self.handle = rope_init(base, head_dim, max_position, self.buf, stream)
 
     def __del__(self):
         if getattr(self, "handle", None):
-            _lib.sfkv_rope_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
 
@@ -194,12 +195,13 @@ class RingCache:
         if n == 0:
             raise ValueError("invalid cache configuration")
         self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self._destroy = _lib.sfkv_cache_destroy    # still reachable at interpreter exit
         self.handle = cache_init(self.cfg, rope.handle, self.buf, stream)
         self.layout = cache_layout(self.handle)
 
     def __del__(self):
         if getattr(self, "handle", None):
-            _lib.sfkv_cache_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
     # compute calls
