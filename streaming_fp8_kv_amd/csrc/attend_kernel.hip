@@ -420,6 +420,10 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) va[db] = read_v(vbuf, 2 * kb, db);
     uint32_t pw[8];
+    // raised wave priority while the score MFMAs are issued: when the other
+    // wave on the SIMD is in its vector phase, the arbiter keeps feeding the
+    // matrix core from this one
+    __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
@@ -433,6 +437,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     const v8h pb0 = __builtin_bit_cast(v8h, (v4u_t){pw[0], pw[1], pw[2], pw[3]});
     const v8h pb1 = __builtin_bit_cast(v8h, (v4u_t){pw[4], pw[5], pw[6], pw[7]});
     v8h vb[NDB];
