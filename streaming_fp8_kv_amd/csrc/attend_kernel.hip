@@ -15,12 +15,14 @@
 //     MFMA 32x32x64;
 //   * keys: raw E4M3 codes staged in LDS, fed unconverted as the A operand, so
 //     each MFMA computes 32 keys x 32 queries over 64 head dims;
-//   * scores come out transposed (keys x queries), in log2 units and already
-//     shifted by the column's reference max; P = exp2(S) in fp16 stays in
-//     registers as the B operand of the fp16 MFMA 32x32x16;
-//   * V is staged in LDS once per tile, converted E4M3 -> fp16 (exact) and
-//     transposed to [dim][key]; O^T accumulates in fp32 and the scale_v / sum
-//     division happens once at the end.
+//   * scores come out transposed (keys x queries), in log2 units;
+//     P = exp2(S - m) in fp16 stays in registers as the B operand of the fp16
+//     MFMA 32x32x16, and its row sums are taken with mixed-precision FMAs (the
+//     dot-product instructions cannot issue while the matrix core is busy);
+//   * V is staged in LDS once per tile, converted E4M3 -> fp16 (exact), in
+//     natural [key][dim] rows; the LDS transpose read (ds_read_b64_tr_b16)
+//     delivers the [dim][key] fragments the PV MFMA needs. O^T accumulates in
+//     fp32 and the scale_v / sum division happens once at the end.
 // A three-term query carries about 12 significant bits and fp16 P about 11,
 // which keeps the result within 1e-3 mean relative error of exact attention on
 // the same FP8 cache; two-term or single-FP8 queries do not. The 32x32 MFMA
@@ -44,17 +46,16 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+typedef short v8s_t __attribute__((ext_vector_type(8)));
 
 constexpr int BK = kAttendKeysPerTile;      // 64 keys per LDS tile
 constexpr int KSTRIDE = 144;                // bytes per key row in LDS (128 + 16 pad)
-// V^T tile in LDS: one 128-byte row per head dim holding 64 keys as 4 groups of
-// 16. Inside a group, key k sits at position 8*bit2(k) + 4*bit3(k) + (k & 3), so
-// the 8 keys one lane of the PV MFMA needs are contiguous (one 16-byte read),
-// and the 16-byte slot s of row d is stored at slot s ^ vswz(d). The swizzle
-// keeps the fragment reads (8 consecutive rows per cycle) free of bank
-// conflicts and the transposing 8-byte stores at most 2-way.
-constexpr int VROW = 64;                    // halfs per dim row (64 keys)
-__device__ __forceinline__ int vswz(int row) { return (row ^ (row >> 3)) & 7; }
+// V tile in LDS: fp16, natural [key][dim] rows of D halfs. The 16-byte chunk c
+// of row r is stored at chunk vchunk(r, c) = c ^ (4 (r & 3)) (within the row), so
+// the transposing fragment reads (four rows x 64 bytes per 32 lanes) and the
+// row stores (16 lanes per row) are both free of bank conflicts at D = 128.
+template <int D>
+__device__ __forceinline__ int vchunk(int row, int c) { return c ^ ((4 * (row & 3)) & (D / 8 - 1)); }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   constexpr int BQB = 128;            // queries per workgroup
   constexpr float kShiftAt = 15.0f;   // P = exp2(s - m_ref) stays <= 2^15, inside fp16
   __shared__ __attribute__((aligned(16))) uint8_t sK[3][BK * KSTRIDE];
-  __shared__ __attribute__((aligned(16))) _Float16 sVt[3][D * VROW];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[3][BK * D];
 
   const int tiles_q = (a.n_q + BQB - 1) / BQB;
   const int n_blocks = tiles_q * a.heads * a.splits;
@@ -295,38 +296,45 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
       *reinterpret_cast<uint4 *>(sK[buf] + key * KSTRIDE + 16 * col) = pk[p];
     }
   };
-  v2h vh[4][4];   // [key j][dim pair] of this thread's V piece
-  auto convert_v = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      vh[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, false);
-      vh[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, true);
-      vh[j][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, false);
-      vh[j][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, true);
-    }
-  };
-  // keys 4kq..4kq+3: group kq/4, 16-byte slot 2(kq/4) + bit0(kq), half bit1(kq)
-  const int v_slot16 = 2 * (v_kq >> 2) + (v_kq & 1), v_half = (v_kq >> 1) & 1;
-  auto store_v = [&](int buf, int dd) {
+  // row 4 v_kq + j has (row & 3) == j; the fp8 -> fp16 widening happens right
+  // before the store, so only the loaded codes stay live between the phases
+  auto store_v = [&](int buf, int j) __attribute__((always_inline)) {
     if (v_role) {
-      const int row = 8 * v_dg + dd;
-      v4h col = {vh[0][dd >> 1][dd & 1], vh[1][dd >> 1][dd & 1], vh[2][dd >> 1][dd & 1], vh[3][dd >> 1][dd & 1]};
-      *reinterpret_cast<v4h *>(sVt[buf] + row * VROW + 8 * (v_slot16 ^ vswz(row)) + 4 * v_half) = col;
+      const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, false);
+      const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, true);
+      const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, false);
+      const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, true);
+      *reinterpret_cast<uint4 *>(sV[buf] + (4 * v_kq + j) * D + 8 * vchunk<D>(j, v_dg)) =
+          uint4{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
     }
   };
 
-  // V^T fragment addressing: for row 32db + r, the 8 keys of PV step m for
-  // this lane sit in 16-byte slot 2m + hh, stored at (hh ^ r ^ (r >> 3)) ^
-  // 2((m ^ 2db) & 3): a per-lane base for each of the 4 values of (m ^ 2db) & 3
-  // plus an immediate row offset.
-  int vbase[4];
+  // V^T fragments through the LDS transpose read (ds_read_b64_tr_b16): in each
+  // 16-lane group, source lane s addresses row 4hh + s/4 (+ the step's key base)
+  // at dims 32db + 16 ((lane >> 4) & 1) + 4 (s & 3), and output lane i receives
+  // element i & 3 of source lanes i/4 + 4j, j = 0..3. So lane l gets the four
+  // keys 4hh + j of dim 32db + (l & 31): MFMA k-slots 8hh + j. A second read 8
+  // keys further on fills k-slots 8hh + 4 + j. Row & 3 = s/4 for every step, so
+  // the swizzle is fixed per lane and per d-block.
+  int vtbase[D / 32];
   {
-    const int mm = (hh ^ r ^ (r >> 3)) & 7;
+    const int s16 = lane & 15, gsub = (lane >> 4) & 1;
+    const int row = 4 * hh + (s16 >> 2);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vbase[k] = r * VROW + 8 * (mm ^ (2 * k));
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 4 * db + 2 * gsub + ((s16 & 3) >> 1);
+      vtbase[db] = 2 * (row * D) + 16 * vchunk<D>(row, c) + 8 * (s16 & 1);
+    }
   }
-  auto read_v = [&](int buf, int m, int db) {
-    return *reinterpret_cast<const v8h *>(sVt[buf] + vbase[(m ^ (2 * db)) & 3] + 32 * db * VROW);
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  auto read_vt = [&](int buf, int key0, int db) __attribute__((always_inline)) {
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(sV[buf]) + vtbase[db] + 2 * key0 * D;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(base));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(base + 2 * 8 * D));
+    return __builtin_bit_cast(v8h, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   };
 
   // K fragments of block kb (32 keys) of buffer buf: the A operand of the score
@@ -355,15 +363,21 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   };
 
   // Online softmax against a reference max m_ref that moves only on the range's
-  // first block or when a score exceeds it by more than 2^15 (so P <= 2^15,
-  // inside fp16). P = exp2(s - m_ref) is rounded to fp16 and the row sum is
-  // taken over the rounded values (dot2 with ones into fp32), so rounding of a
-  // dominant weight cancels between numerator and denominator.
-  float m_ref = kNegBig, l_run = 0.0f;
+  // first block or when a block's max exceeds it by more than 15 in log2 units
+  // (so P <= 2^15, inside fp16). P = exp2(s - m_ref) is rounded to fp16 and the
+  // row sum is taken over the rounded values (exactly, in fp32), so rounding of
+  // a dominant weight cancels between numerator and denominator.
+  float m_ref = kNegBig, l_run = 0.0f, l_run2 = 0.0f;
   v16f oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = v16f{};
-  const v2h ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  // Row sums += both fp16 weights of w, exactly (mixed-precision FMA by 1.0):
+  // two partial sums, and no dot-product instruction, which cannot issue while
+  // the matrix core is busy.
+  auto add_pair = [&](uint32_t w) {
+    asm volatile("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(l_run) : "v"(w));
+    asm volatile("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l_run2) : "v"(w));
+  };
 
   // Maximum of a block's 32 scores per query column (both wave halves).
   auto block_max = [&](const v16f &s) {
@@ -386,6 +400,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
+      l_run2 *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
@@ -396,10 +411,10 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
         (float2_t){__builtin_amdgcn_exp2f(s[i0] - m_ref), __builtin_amdgcn_exp2f(s[i0 + 1] - m_ref)}, v2h);
     const v2h b = __builtin_convertvector(
         (float2_t){__builtin_amdgcn_exp2f(s[i0 + 2] - m_ref), __builtin_amdgcn_exp2f(s[i0 + 3] - m_ref)}, v2h);
-    l_run = __builtin_amdgcn_fdot2(a, ones, l_run, false);
-    l_run = __builtin_amdgcn_fdot2(b, ones, l_run, false);
     w[0] = __builtin_bit_cast(uint32_t, a);
     w[1] = __builtin_bit_cast(uint32_t, b);
+    add_pair(w[0]);
+    add_pair(w[1]);
   };
 
   // One region per block, written in issue order with scheduling fences so that
@@ -418,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
     read_k(qbuf, qkb, kf);
     v8h va[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) va[db] = read_v(vbuf, 2 * kb, db);
+    for (int db = 0; db < NDB; ++db) va[db] = read_vt(vbuf, 32 * kb, db);
     uint32_t pw[8];
     // raised wave priority while the score MFMAs are issued: when the other
     // wave on the SIMD is in its vector phase, the arbiter keeps feeding the
@@ -433,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
       if (i == NQK - 1) {
 #pragma unroll
         for (int g = NQK; g < 4; ++g) exp4(s_cur, 4 * g, pw + 2 * g);
-        if (stage) { store_k(sbuf); convert_v(); }
+        if (stage) store_k(sbuf);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -442,24 +457,17 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
     const v8h pb1 = __builtin_bit_cast(v8h, (v4u_t){pw[4], pw[5], pw[6], pw[7]});
     v8h vb[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) vb[db] = read_v(vbuf, 2 * kb + 1, db);
-    constexpr int SPER = 8 / (2 * NDB);   // V column stores per PV MFMA
+    for (int db = 0; db < NDB; ++db) vb[db] = read_vt(vbuf, 32 * kb + 16, db);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db], pb0, oacc[db], 0, 0, 0);
-      if (stage) {
-#pragma unroll
-        for (int k = 0; k < SPER; ++k) store_v(sbuf, db * SPER + k);
-      }
+      if (stage && db < 4) store_v(sbuf, db);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db], pb1, oacc[db], 0, 0, 0);
-      if (stage) {
-#pragma unroll
-        for (int k = 0; k < SPER; ++k) store_v(sbuf, (NDB + db) * SPER + k);
-      }
+      if (stage && NDB + db < 4) store_v(sbuf, NDB + db);
       if (db == NDB - 1) tmax_next = block_max(s_next);   // in the shadow of the PV MFMAs
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -469,9 +477,8 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
     // Prologue: tile 0 in buffer 0, tile 1 in registers, scores of block 0.
     load_tile(kbeg);
     store_k(0);
-    convert_v();
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) store_v(0, dd);
+    for (int j = 0; j < 4; ++j) store_v(0, j);
     load_tile(kbeg + BK);                          // past the range reads zeros
     __syncthreads();
     v16f s0, s1;
@@ -508,6 +515,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 
   // ---- epilogue ---------------------------------------------------------------
   // register i of d-block db holds dim 32db + 8(i/4) + 4hh + (i%4)
+  l_run += l_run2;
   const float l_tot = l_run + other_half(l_run);
   if (qi >= a.n_q) return;
   if (a.splits == 1) {

@@ -177,35 +177,54 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibrateLaunch a) {
   }
 }
 
-// One thread = 16 code bytes (8 pairs) of one valid (head, slot) row: decode
-// exactly to fp32, rotate by -delta, clamp, re-encode, store in place. The
-// per-head scale cancels because the rotation is linear.
+// Delta rotation of the cached keys, one head per grid row. A thread owns one
+// 16-byte column chunk (8 code pairs) and two rows of its wave's slab, so its 8
+// cos/sin pairs are loaded once per two rows and both 16-byte loads are in
+// flight before the first store. The lanes of a wave cover 64 / (D/16)
+// consecutive rows completely at each step, so every load and store is one
+// contiguous kilobyte per wave. Each code pair is decoded exactly to fp32,
+// rotated by -delta, clamped and re-encoded in place; the per-head scale
+// cancels because the rotation is linear.
+template <int D>
 __global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunch a) {
-  const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 4;
-  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const unsigned total = static_cast<unsigned>(a.heads) * a.n_valid * chunks;
-  if (idx >= total) return;
-  const int c = static_cast<int>(idx % chunks);
-  const unsigned row = idx / chunks;
-  const int slot = static_cast<int>(row % static_cast<unsigned>(a.n_valid));
-  const int h = static_cast<int>(row / static_cast<unsigned>(a.n_valid));
-  uint8_t *ptr = a.k8 + (static_cast<size_t>(h) * a.capacity + slot) * a.head_dim + c * 16;
-  uint4 w = *reinterpret_cast<const uint4 *>(ptr);
-  float x[16];
-  decode4(w.x, x);
-  decode4(w.y, x + 4);
-  decode4(w.z, x + 8);
-  decode4(w.w, x + 12);
+  constexpr int CH = D / 16;            // 16-byte chunks per row
+  constexpr int RSTEP = 64 / CH;        // rows one wave covers per step
+  constexpr int J = 2;                  // steps per thread
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane % CH;
+  const int slot0 = (blockIdx.x * 4 + wave) * (RSTEP * J) + lane / CH;
+  uint8_t *base = a.k8 + static_cast<size_t>(h) * a.capacity * D + c * 16;
   const RopePair *cs = a.rope_row + c * 8;
+  RopePair t[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) rotate_pair_back(x[2 * j], x[2 * j + 1], cs[j]);
-  uint4 o;
-  o.x = encode4(x[0], x[1], x[2], x[3]);
-  o.y = encode4(x[4], x[5], x[6], x[7]);
-  o.z = encode4(x[8], x[9], x[10], x[11]);
-  o.w = encode4(x[12], x[13], x[14], x[15]);
-  *reinterpret_cast<uint4 *>(ptr) = o;
-  if (h == 0 && c == 0) a.pos[slot] -= a.delta;
+  for (int k = 0; k < 8; ++k) t[k] = cs[k];
+  uint4 w[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int slot = slot0 + j * RSTEP;
+    if (slot < a.n_valid) w[j] = *reinterpret_cast<const uint4 *>(base + static_cast<size_t>(slot) * D);
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int slot = slot0 + j * RSTEP;
+    if (slot < a.n_valid) {
+      float x[16];
+      decode4(w[j].x, x);
+      decode4(w[j].y, x + 4);
+      decode4(w[j].z, x + 8);
+      decode4(w[j].w, x + 12);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rotate_pair_back(x[2 * k], x[2 * k + 1], t[k]);
+      uint4 o;
+      o.x = encode4(x[0], x[1], x[2], x[3]);
+      o.y = encode4(x[4], x[5], x[6], x[7]);
+      o.z = encode4(x[8], x[9], x[10], x[11]);
+      o.w = encode4(x[12], x[13], x[14], x[15]);
+      *reinterpret_cast<uint4 *>(base + static_cast<size_t>(slot) * D) = o;
+      if (h == 0 && c == 0) a.pos[slot] -= a.delta;
+    }
+  }
 }
 
 inline unsigned blocks_for(size_t threads, unsigned per_block) {
@@ -227,9 +246,13 @@ hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s) {
-  const size_t threads = static_cast<size_t>(a.heads) * a.n_valid * (a.head_dim >> 4);
-  if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(rebase_kernel, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
+  if (a.n_valid <= 0 || a.heads <= 0) return hipSuccess;
+  // rows per workgroup: 4 waves x (64 / (D/16)) rows x 2 steps
+  const int rows_per_block = 4 * (64 / (a.head_dim / 16)) * 2;
+  const dim3 grid(static_cast<unsigned>((a.n_valid + rows_per_block - 1) / rows_per_block),
+                  static_cast<unsigned>(a.heads));
+  if (a.head_dim == 128) hipLaunchKernelGGL(rebase_kernel<128>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(rebase_kernel<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -93,6 +93,29 @@ def test_long_session_with_resets(sfkv):
     assert m.ora.next_pos == (spec.steps - 168) * 757
 
 
+def test_rebase_partial_ring_all_heads(sfkv):
+    """Delta rotation before the ring wraps (3 frames = 2,271 valid slots, not a
+    multiple of any launch tile), checked on all 24 heads: a small delta, then a
+    reset to position 0, each followed by a write and an attention check."""
+    spec = W.PROD
+    say("case rebase_partial_h24_d128_n757_c5788")
+    m = Mirror(sfkv, rope_for(sfkv, spec.shape), spec)
+    fs = W.FrameStream(spec)
+    for step in range(3):
+        q, k, v = fs.frame()
+        if step == 0:
+            m.calibrate(k, v)
+        m.write(k, v)
+    assert m.gpu.state()["n_valid"] == 3 * 757
+    for delta in (5, None):
+        m.rebase(m.ora.next_pos if delta is None else delta)
+        m.check_cache(f"after rebase {delta}")
+        q, k, v = fs.frame()
+        m.write(k, v)
+        m.check_cache(f"write after rebase {delta}")
+        m.check_attend(q, rows=spread_rows(q.shape[0], 32), tag=f"attend after rebase {delta}")
+
+
 def test_stress_heavy_tails_variable_first_write(sfkv):
     """40 heads, Student-t(3) keys and values with per-head std up to 8 (so later
     frames saturate the E4M3 range of the step-0 scales), a first write of
