@@ -18,8 +18,11 @@ is up to three kernel launches (query prep, attention, split combine); the
 rocprofv3 summary lists each. cache_write alone, the same
 step captured once as a HIP graph and replayed, and the position reset (one
 delta rotation per cache) are timed in separate regions after the timed one and
-reported under ``extra``. ``cpu_baseline`` times the CPU oracle on a bounded
-sample.
+reported under ``extra``. So is the launch software's plain path on a sample of
+caches (``plain_*``): per call, the raw window is copy-shifted and every cached
+key re-rotated and re-quantised before the same attention, which is the upkeep
+the ring and write-time RoPE remove ("Where the Time Went"). ``cpu_baseline``
+times the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -50,6 +53,8 @@ def parse():
     ap.add_argument("--calls", type=int, default=240, help="caches (calls) per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-calls", type=int, default=32)
+    ap.add_argument("--plain-calls", type=int, default=24,
+                    help="caches for the plain-path (linear window) comparison; 0 skips it")
     return ap.parse_args()
 
 
@@ -86,6 +91,46 @@ def cpu_baseline(n_calls: int):
             "sample": f"{n_calls} production calls (757 new tokens, 5,788-slot wrapped ring, "
                       f"24 heads x 128, fp64 attention over all rows) after an untimed 8-frame prefill; "
                       f"{dt:.1f} s of CPU time"}
+
+
+def plain_path(sfkv, W, spec, n_caches: int, stream):
+    """The launch software's cache on `n_caches` caches of the production shape:
+    each window is filled with 8 frames, then one write (copy-shift + rotate and
+    re-quantise the whole window) and one attend per cache are timed with events
+    around each call. Inputs are drawn on the device before timing."""
+    import torch
+    s = spec.shape
+    E = torch.cuda.Event
+    rope = sfkv.Rope(s.head_dim, s.max_position, s.rope_base)
+    caches, last = [], []
+    for i in range(n_caches):
+        fs = W.FrameStream(spec, seed=spec.seed * 1000 + 500 + i, device="cuda")
+        c = sfkv.LinearCache(rope, s.heads, s.capacity, s.new_tokens)
+        for f in range(spec.prefill_frames):
+            q, k, v = fs.frame(s.new_tokens)
+            if f == 0:
+                c.calibrate_scales(k, v, stream)
+            c.cache_write(k, v, stream)
+        caches.append(c)
+        last.append(fs.frame(s.new_tokens))
+    ws = torch.empty(caches[0].workspace_bytes(), dtype=torch.uint8, device="cuda")
+    out = torch.empty(s.new_tokens, s.heads, s.head_dim, dtype=torch.float32, device="cuda")
+    for c, (q, k, v) in zip(caches, last):          # warm-up: one steady-state call each
+        c.cache_write(k, v, stream)
+        c.attend(q, out, ws, stream)
+    ev = [(E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)) for _ in caches]
+    torch.cuda.synchronize()
+    for c, (q, k, v), (a, b, e) in zip(caches, last, ev):
+        a.record(stream)
+        c.cache_write(k, v, stream)
+        b.record(stream)
+        c.attend(q, out, ws, stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    upkeep = sum(a.elapsed_time(b) for a, b, _ in ev) * 1e3 / len(ev)
+    attend = sum(b.elapsed_time(e) for _, b, e in ev) * 1e3 / len(ev)
+    del caches
+    return {"upkeep_us": upkeep, "attend_us": attend}
 
 
 def main():
@@ -180,6 +225,8 @@ def main():
     torch.cuda.synchronize()
     rebase_us = sum(a.elapsed_time(b) for a, b in rb) * 1e3 / len(rb)
 
+    plain = plain_path(sfkv, W, spec, args.plain_calls, stream) if args.plain_calls > 0 else None
+
     n, H, d, C = s.new_tokens, s.heads, s.head_dim, s.capacity
     attend_flops = 4.0 * n * C * H * d
     write_bytes = 2 * n * H * d * 2 + 2 * n * H * d * 1
@@ -215,8 +262,17 @@ def main():
             "reset_step_extra_ms": round(rebase_us * n_calls / 1e3, 4),
             "graph_ms_per_step": round(graph_ms, 4),
             "graph_us_per_call": round(graph_ms * 1e3 / n_calls, 3),
+            "ring_upkeep_ms_per_step": round(write_us * n_calls / 1e3, 4),
         },
     }
+    if plain is not None:
+        line["extra"].update({
+            "plain_calls_sampled": args.plain_calls,
+            "plain_upkeep_us": round(plain["upkeep_us"], 3),
+            "plain_attend_us": round(plain["attend_us"], 3),
+            "plain_us_per_call": round(plain["upkeep_us"] + plain["attend_us"], 3),
+            "plain_upkeep_ms_per_step": round(plain["upkeep_us"] * n_calls / 1e3, 4),
+        })
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_sample_calls)

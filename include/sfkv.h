@@ -168,6 +168,51 @@ sfkv_status sfkv_cache_state(const sfkv_cache *cache, int64_t *tokens, int64_t *
 sfkv_status sfkv_cache_layout(const sfkv_cache *cache, size_t *k_off, size_t *v_off,
                               size_t *pos_off, size_t *scale_off);
 
+/* ---- Launch-software path (plain linear window) --------------------------
+ * The cache as the launch software kept it ("Where the Time Went"): a
+ * time-ordered window of the last `capacity` raw (unrotated) tokens in the
+ * input dtype, advanced by copying; on every write the whole window is rotated
+ * at window positions 0 .. m-1 and re-quantised into FP8 planes with the
+ * per-head scales; attention reads those planes. It is kept as the plain code
+ * path behind the same kind of interface ("What Broke in Production": every
+ * optimisation sits behind a switch that keeps the plain path) and to measure
+ * the per-call upkeep that write-time RoPE and the ring remove. Attention
+ * depends only on query-key position differences, so in exact arithmetic it
+ * equals the ring's result for the same tokens.
+ *
+ * sfkv_linear_bytes / sfkv_linear_init: as sfkv_cache_bytes / sfkv_cache_init,
+ * with the window dtype fixed at init (k, v, q of later calls use it). The
+ * buffer holds the FP8 planes, positions and scales at the offsets
+ * sfkv_linear_layout() reports, then two raw windows of
+ * capacity * num_heads * head_dim elements per tensor. The rope table must
+ * cover positions 0 .. capacity (ERANGE otherwise).
+ * sfkv_linear_calibrate_scales: per-head scales from one frame, as
+ * sfkv_calibrate_scales, with keys rotated at the window positions the frame
+ * would take if written now (0 .. n-1 for the first frame).
+ * sfkv_linear_write: copy the kept rows of the window and the new frame into
+ * the other window (dropping the oldest rows beyond capacity), then rotate and
+ * quantise all m = min(tokens, capacity) rows into the planes; positions[i] = i.
+ * sfkv_linear_attend: as sfkv_attend over the m window slots, queries at window
+ * positions m - n_q .. m - 1 (n_q must equal the last write's n_tokens).
+ * Errors as for the ring calls; ESTATE for a write before calibration or an
+ * attend before a write. */
+typedef struct sfkv_linear sfkv_linear;  /* host handle; window in caller device memory */
+size_t sfkv_linear_bytes(const sfkv_cache_cfg *cfg, sfkv_dtype dtype);
+sfkv_status sfkv_linear_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, sfkv_dtype dtype,
+                             void *dev_mem, size_t bytes, void *stream, sfkv_linear **out);
+void sfkv_linear_destroy(sfkv_linear *cache);
+sfkv_status sfkv_linear_calibrate_scales(sfkv_linear *cache, const void *k, const void *v,
+                                         int32_t n_tokens, void *stream);
+sfkv_status sfkv_linear_write(sfkv_linear *cache, const void *k, const void *v, int32_t n_tokens,
+                              void *stream);
+size_t sfkv_linear_workspace_bytes(const sfkv_linear *cache);
+sfkv_status sfkv_linear_attend(sfkv_linear *cache, const void *q, int32_t n_q, float *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+/* n_window: tokens in the window (m); last_n: n_tokens of the last write. */
+sfkv_status sfkv_linear_state(const sfkv_linear *cache, int32_t *n_window, int32_t *last_n);
+sfkv_status sfkv_linear_layout(const sfkv_linear *cache, size_t *k_off, size_t *v_off,
+                               size_t *pos_off, size_t *scale_off);
+
 const char *sfkv_status_string(sfkv_status status);
 const char *sfkv_last_error(void);
 

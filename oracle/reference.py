@@ -72,6 +72,16 @@ class LinearCache:
         self.v = np.concatenate([self.v, v])[-self.C:].copy()
         self.last_n = k.shape[0]
 
+    def quantized_window(self):
+        """FP8 codes of the whole window as the call re-creates them (mode 'fp8'):
+        keys rotated in fp32 at window positions 0 .. m-1, then both tensors
+        quantised with the per-head scales. Returns ``(k8, v8)``, each ``[m,H,d]``."""
+        m = self.k.shape[0]
+        sk, ik, sv, iv = self.scales
+        c, s = rope.cos_sin(np.arange(m), self.d, self.base)
+        kr = rope.rotate(self.k, c[:, None, :], s[:, None, :])
+        return e4m3.quantize(kr, ik[None, :, None]), e4m3.quantize(self.v, iv[None, :, None])
+
     def attend(self, q, rows=None):
         q = np.asarray(q, dtype=np.float32)
         m = self.k.shape[0]
@@ -84,10 +94,7 @@ class LinearCache:
             vv = np.transpose(self.v.astype(np.float64), (1, 0, 2))
         else:
             sk, ik, sv, iv = self.scales
-            c, s = rope.cos_sin(kpos, self.d, self.base)
-            kr = rope.rotate(self.k, c[:, None, :], s[:, None, :])
-            k8 = e4m3.quantize(kr, ik[None, :, None])
-            v8 = e4m3.quantize(self.v, iv[None, :, None])
+            k8, v8 = self.quantized_window()
             kk = np.transpose(e4m3.decode(k8) * sk.astype(np.float64)[None, :, None], (1, 0, 2))
             vv = np.transpose(e4m3.decode(v8) * sv.astype(np.float64)[None, :, None], (1, 0, 2))
             c, s = rope.cos_sin(qpos, self.d, self.base)

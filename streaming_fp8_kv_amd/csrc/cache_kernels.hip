@@ -227,6 +227,22 @@ __global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunch a) {
   }
 }
 
+// Window shift of the launch software's linear cache ("Where the Time Went":
+// the window was advanced by copying it): one thread per 16-byte unit of the
+// new window, blockIdx.y selects K (0) or V (1).
+__global__ __launch_bounds__(256) void shift_kernel(ShiftLaunch a) {
+  const size_t per_row = a.row_bytes / 16;
+  const size_t u = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (u >= static_cast<size_t>(a.kept + a.n) * per_row) return;
+  const size_t row = u / per_row, col = u - row * per_row;
+  const bool is_v = blockIdx.y != 0;
+  const uint8_t *src = row < static_cast<size_t>(a.kept)
+                           ? (is_v ? a.old_v : a.old_k) + (row + a.drop) * a.row_bytes
+                           : (is_v ? a.frame_v : a.frame_k) + (row - a.kept) * a.row_bytes;
+  uint8_t *dst = (is_v ? a.dst_v : a.dst_k) + row * a.row_bytes;
+  reinterpret_cast<uint4 *>(dst)[col] = reinterpret_cast<const uint4 *>(src)[col];
+}
+
 inline unsigned blocks_for(size_t threads, unsigned per_block) {
   return static_cast<unsigned>((threads + per_block - 1) / per_block);
 }
@@ -237,6 +253,13 @@ hipError_t launch_write(const WriteLaunch &a, hipStream_t s) {
   const size_t threads = static_cast<size_t>(a.n) * a.heads * (a.head_dim >> 4);
   if (a.dtype == 0) hipLaunchKernelGGL(write_kernel<0>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(write_kernel<1>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shift(const ShiftLaunch &a, hipStream_t s) {
+  const size_t units = static_cast<size_t>(a.kept + a.n) * (a.row_bytes / 16);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(shift_kernel, dim3(blocks_for(units, 256), 2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

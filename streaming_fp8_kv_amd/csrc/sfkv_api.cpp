@@ -280,20 +280,20 @@ size_t sfkv_attend_workspace_bytes(const sfkv_cache *c) {
   return attend_ws(c->cfg).total;
 }
 
-sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t n_q, float *out,
-                        void *workspace, size_t workspace_bytes, void *stream) {
-  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
-  if (c->last_n == 0) return fail(SFKV_ESTATE, "attend before any cache_write");
+// One attend launch over FP8 planes laid out as layout_of(cfg) at `base`:
+// n_valid slots, queries at positions qpos0 .. qpos0 + n_q - 1.
+static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, const sfkv_rope *rope, uint8_t *base,
+                                 int nv, int64_t qpos0, const void *q, sfkv_dtype dtype, int32_t n_q,
+                                 float *out, void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !out) return fail(SFKV_EINVAL, "q and out must be device pointers");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(SFKV_EINVAL, "q and out must be 16-byte aligned");
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
-  if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
-  const int nv = n_valid_of(c);
-  const AttendWs ws = attend_ws(c->cfg);
+  const AttendWs ws = attend_ws(cfg);
   if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 256))
-    return fail(SFKV_EINVAL, "workspace missing, smaller than sfkv_attend_workspace_bytes() or not 256-byte aligned");
-  const size_t rows_per_split = static_cast<size_t>(n_q) * c->cfg.num_heads;
-  int splits = sfkv::attend_splits(n_q, c->cfg.num_heads, nv);
+    return fail(SFKV_EINVAL, "workspace missing, smaller than the attend workspace size or not 256-byte aligned");
+  const Layout l = layout_of(cfg);
+  const size_t rows_per_split = static_cast<size_t>(n_q) * cfg.num_heads;
+  int splits = sfkv::attend_splits(n_q, cfg.num_heads, nv);
   if (splits > 1 && static_cast<size_t>(splits) * rows_per_split > ws.rows_cap)
     splits = static_cast<int>(ws.rows_cap / rows_per_split);
   if (splits < 2) splits = 1;
@@ -301,15 +301,15 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   a.q = q;
   a.dtype = dtype;
   a.n_q = n_q;
-  a.heads = c->cfg.num_heads;
-  a.head_dim = c->cfg.head_dim;
-  a.capacity = c->cfg.capacity;
+  a.heads = cfg.num_heads;
+  a.head_dim = cfg.head_dim;
+  a.capacity = cfg.capacity;
   a.n_valid = nv;
-  a.qpos0 = static_cast<int>(c->last_pos0);
-  a.rope = c->rope->table;
-  a.k8 = c->base + c->k_off;
-  a.v8 = c->base + c->v_off;
-  a.scales = reinterpret_cast<const float *>(c->base + c->scale_off);
+  a.qpos0 = static_cast<int>(qpos0);
+  a.rope = rope->table;
+  a.k8 = base + l.k;
+  a.v8 = base + l.v;
+  a.scales = reinterpret_cast<const float *>(base + l.scale);
   a.out = out;
   a.splits = splits;
   uint8_t *wsb = static_cast<uint8_t *>(workspace);
@@ -318,6 +318,15 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   a.part_o = splits > 1 ? reinterpret_cast<float *>(wsb + ws.part_o) : nullptr;
   a.part_ml = splits > 1 ? reinterpret_cast<float *>(wsb + ws.part_ml) : nullptr;
   return launched(sfkv::launch_attend(a, as_stream(stream)));
+}
+
+sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t n_q, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (c->last_n == 0) return fail(SFKV_ESTATE, "attend before any cache_write");
+  if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
+  return attend_planes(c->cfg, c->rope, c->base, n_valid_of(c), c->last_pos0, q, dtype, n_q, out,
+                       workspace, workspace_bytes, stream);
 }
 
 sfkv_status sfkv_rebase_positions(sfkv_cache *c, int64_t delta, void *stream) {
@@ -361,6 +370,196 @@ sfkv_status sfkv_cache_layout(const sfkv_cache *c, size_t *k_off, size_t *v_off,
   if (v_off) *v_off = c->v_off;
   if (pos_off) *pos_off = c->pos_off;
   if (scale_off) *scale_off = c->scale_off;
+  return ok();
+}
+
+// ---- launch-software (linear window) cache ------------------------------------
+// Device buffer: the FP8 planes, positions and scales exactly as layout_of(cfg),
+// then two raw windows (K then V, [capacity][heads][head_dim] of the input
+// dtype each). A write copies the kept rows of the current window and the new
+// frame into the other window, then rotates and quantises the whole new window
+// into the planes at window positions 0 .. m-1.
+struct sfkv_linear {
+  sfkv_cache_cfg cfg;
+  const sfkv_rope *rope;
+  sfkv_dtype dtype;
+  uint8_t *base;
+  size_t win_off[2];
+  size_t win_bytes;      // one tensor (K or V) of one window
+  size_t total;
+  int32_t m;             // tokens in the window
+  int32_t last_n;
+  int cur;               // window holding the current tokens
+  bool calibrated;
+};
+
+namespace {
+
+size_t elem_size(sfkv_dtype d) { return d == SFKV_FP32 ? 4 : 2; }
+
+struct LinearLayout {
+  Layout planes;
+  size_t win[2], win_bytes, total;
+};
+
+LinearLayout linear_layout_of(const sfkv_cache_cfg &c, sfkv_dtype dtype) {
+  LinearLayout l;
+  l.planes = layout_of(c);
+  l.win_bytes = static_cast<size_t>(c.capacity) * c.num_heads * c.head_dim * elem_size(dtype);
+  l.win[0] = l.planes.total;
+  l.win[1] = align_up(l.win[0] + 2 * l.win_bytes, 256);
+  l.total = align_up(l.win[1] + 2 * l.win_bytes, 256);
+  return l;
+}
+
+sfkv_status check_linear_frame(const sfkv_linear *c, const void *k, const void *v, int32_t n) {
+  if (!c) return fail(SFKV_EINVAL, "linear cache is NULL");
+  if (!k || !v) return fail(SFKV_EINVAL, "k and v must be device pointers");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(SFKV_EINVAL, "k and v must be 16-byte aligned");
+  if (n < 1 || n > c->cfg.max_new_tokens) return fail(SFKV_EINVAL, "n_tokens must be in [1, max_new_tokens]");
+  return SFKV_OK;
+}
+
+}  // namespace
+
+size_t sfkv_linear_bytes(const sfkv_cache_cfg *cfg, sfkv_dtype dtype) {
+  if (check_cfg(cfg) != SFKV_OK) return 0;
+  if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return 0;
+  return linear_layout_of(*cfg, dtype).total;
+}
+
+sfkv_status sfkv_linear_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, sfkv_dtype dtype,
+                             void *dev_mem, size_t bytes, void *stream, sfkv_linear **out) {
+  if (!out) return fail(SFKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  sfkv_status st = check_cfg(cfg);
+  if (st != SFKV_OK) return st;
+  if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
+  if (!rope) return fail(SFKV_EINVAL, "rope is NULL");
+  if (rope->head_dim != cfg->head_dim) return fail(SFKV_EINVAL, "rope head_dim differs from cfg head_dim");
+  if (rope->max_position < cfg->capacity)
+    return fail(SFKV_ERANGE, "the rope table must cover window positions 0 .. capacity - 1");
+  const LinearLayout l = linear_layout_of(*cfg, dtype);
+  if (!dev_mem || !aligned(dev_mem, 256)) return fail(SFKV_EINVAL, "dev_mem must be 256-byte aligned device memory");
+  if (bytes < l.total) return fail(SFKV_EINVAL, "dev_mem smaller than sfkv_linear_bytes()");
+  hipError_t e = hipMemsetAsync(dev_mem, 0, l.planes.total, as_stream(stream));
+  if (e != hipSuccess) return fail(SFKV_EHIP, std::string("cache clear failed: ") + hipGetErrorString(e));
+  sfkv_linear *c = new (std::nothrow) sfkv_linear;
+  if (!c) return fail(SFKV_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->rope = rope;
+  c->dtype = dtype;
+  c->base = static_cast<uint8_t *>(dev_mem);
+  c->win_off[0] = l.win[0];
+  c->win_off[1] = l.win[1];
+  c->win_bytes = l.win_bytes;
+  c->total = l.total;
+  c->m = 0;
+  c->last_n = 0;
+  c->cur = 0;
+  c->calibrated = false;
+  *out = c;
+  return ok();
+}
+
+void sfkv_linear_destroy(sfkv_linear *c) { delete c; }
+
+sfkv_status sfkv_linear_calibrate_scales(sfkv_linear *c, const void *k, const void *v, int32_t n,
+                                         void *stream) {
+  sfkv_status st = check_linear_frame(c, k, v, n);
+  if (st != SFKV_OK) return st;
+  const int32_t new_m = c->m + n < c->cfg.capacity ? c->m + n : c->cfg.capacity;
+  const Layout l = layout_of(c->cfg);
+  sfkv::CalibrateLaunch a;
+  a.k = k;
+  a.v = v;
+  a.dtype = c->dtype;
+  a.n = n;
+  a.heads = c->cfg.num_heads;
+  a.head_dim = c->cfg.head_dim;
+  a.pos0 = new_m - n;              // the window positions this frame would take
+  a.rope = c->rope->table;
+  a.scales = reinterpret_cast<float *>(c->base + l.scale);
+  st = launched(sfkv::launch_calibrate(a, as_stream(stream)));
+  if (st == SFKV_OK) c->calibrated = true;
+  return st;
+}
+
+sfkv_status sfkv_linear_write(sfkv_linear *c, const void *k, const void *v, int32_t n, void *stream) {
+  sfkv_status st = check_linear_frame(c, k, v, n);
+  if (st != SFKV_OK) return st;
+  if (!c->calibrated) return fail(SFKV_ESTATE, "linear_write before linear_calibrate_scales");
+  const int32_t new_m = c->m + n < c->cfg.capacity ? c->m + n : c->cfg.capacity;
+  const int32_t drop = c->m + n - new_m;
+  const int nxt = 1 - c->cur;
+  const size_t row = static_cast<size_t>(c->cfg.num_heads) * c->cfg.head_dim * elem_size(c->dtype);
+  sfkv::ShiftLaunch s;
+  s.old_k = c->base + c->win_off[c->cur];
+  s.old_v = c->base + c->win_off[c->cur] + c->win_bytes;
+  s.frame_k = static_cast<const uint8_t *>(k);
+  s.frame_v = static_cast<const uint8_t *>(v);
+  s.dst_k = c->base + c->win_off[nxt];
+  s.dst_v = c->base + c->win_off[nxt] + c->win_bytes;
+  s.row_bytes = row;
+  s.drop = drop;
+  s.kept = c->m - drop;
+  s.n = n;
+  st = launched(sfkv::launch_shift(s, as_stream(stream)));
+  if (st != SFKV_OK) return st;
+  // rotate and quantise the whole window at positions 0 .. new_m - 1
+  const Layout l = layout_of(c->cfg);
+  sfkv::WriteLaunch a;
+  a.k = s.dst_k;
+  a.v = s.dst_v;
+  a.dtype = c->dtype;
+  a.n = new_m;
+  a.heads = c->cfg.num_heads;
+  a.head_dim = c->cfg.head_dim;
+  a.capacity = c->cfg.capacity;
+  a.slot0 = 0;
+  a.pos0 = 0;
+  a.rope = c->rope->table;
+  a.k8 = c->base + l.k;
+  a.v8 = c->base + l.v;
+  a.pos = reinterpret_cast<int32_t *>(c->base + l.pos);
+  a.scales = reinterpret_cast<const float *>(c->base + l.scale);
+  st = launched(sfkv::launch_write(a, as_stream(stream)));
+  if (st != SFKV_OK) return st;
+  c->cur = nxt;
+  c->m = new_m;
+  c->last_n = n;
+  return SFKV_OK;
+}
+
+size_t sfkv_linear_workspace_bytes(const sfkv_linear *c) {
+  if (!c) return 0;
+  return attend_ws(c->cfg).total;
+}
+
+sfkv_status sfkv_linear_attend(sfkv_linear *c, const void *q, int32_t n_q, float *out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (!c) return fail(SFKV_EINVAL, "linear cache is NULL");
+  if (c->last_n == 0) return fail(SFKV_ESTATE, "linear_attend before any linear_write");
+  if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last linear_write");
+  return attend_planes(c->cfg, c->rope, c->base, c->m, c->m - c->last_n, q, c->dtype, n_q, out,
+                       workspace, workspace_bytes, stream);
+}
+
+sfkv_status sfkv_linear_state(const sfkv_linear *c, int32_t *n_window, int32_t *last_n) {
+  if (!c) return fail(SFKV_EINVAL, "linear cache is NULL");
+  if (n_window) *n_window = c->m;
+  if (last_n) *last_n = c->last_n;
+  return ok();
+}
+
+sfkv_status sfkv_linear_layout(const sfkv_linear *c, size_t *k_off, size_t *v_off, size_t *pos_off,
+                               size_t *scale_off) {
+  if (!c) return fail(SFKV_EINVAL, "linear cache is NULL");
+  const Layout l = layout_of(c->cfg);
+  if (k_off) *k_off = l.k;
+  if (v_off) *v_off = l.v;
+  if (pos_off) *pos_off = l.pos;
+  if (scale_off) *scale_off = l.scale;
   return ok();
 }
 

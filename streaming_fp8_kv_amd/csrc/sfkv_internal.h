@@ -53,6 +53,18 @@ struct AttendLaunch {
   uint32_t *qscale;          // [n_q][heads][head_dim/32] E8M0 scales, byte t = term t
 };
 
+// Copy-shift of a linear window (the launch software's cache): destination rows
+// [0, kept) come from old rows [drop, drop + kept), rows [kept, kept + n) from
+// the new frame; rows are row_bytes long (a multiple of 16), K and V alike.
+struct ShiftLaunch {
+  const uint8_t *old_k, *old_v;
+  const uint8_t *frame_k, *frame_v;
+  uint8_t *dst_k, *dst_v;
+  size_t row_bytes;
+  int drop, kept, n;
+};
+
+hipError_t launch_shift(const ShiftLaunch &a, hipStream_t s);
 hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s);
 hipError_t launch_write(const WriteLaunch &a, hipStream_t s);
 hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s);

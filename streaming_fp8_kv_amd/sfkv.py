@@ -8,8 +8,12 @@ is no fallback implementation.
 The function names mirror the C entry points without their ``sfkv_`` prefix:
 ``rope_bytes``, ``rope_init``, ``cache_bytes``, ``cache_init``,
 ``calibrate_scales``, ``cache_write``, ``attend_workspace_bytes``, ``attend``,
-``rebase_positions``, ``cache_state``, ``cache_layout``. ``Rope`` and
-``RingCache`` bundle a handle with the torch buffer it lives in.
+``rebase_positions``, ``cache_state``, ``cache_layout``, and for the launch
+software's plain linear window ``linear_bytes``, ``linear_init``,
+``linear_calibrate_scales``, ``linear_write``, ``linear_workspace_bytes``,
+``linear_attend``, ``linear_state``, ``linear_layout``. ``Rope``,
+``RingCache`` and ``LinearCache`` bundle a handle with the torch buffer it
+lives in.
 """
 from __future__ import annotations
 
@@ -35,7 +39,11 @@ SYMBOLS = (
     "sfkv_cache_bytes", "sfkv_cache_init", "sfkv_cache_destroy",
     "sfkv_calibrate_scales", "sfkv_cache_write",
     "sfkv_attend_workspace_bytes", "sfkv_attend", "sfkv_rebase_positions",
-    "sfkv_cache_state", "sfkv_cache_layout", "sfkv_status_string", "sfkv_last_error",
+    "sfkv_cache_state", "sfkv_cache_layout",
+    "sfkv_linear_bytes", "sfkv_linear_init", "sfkv_linear_destroy",
+    "sfkv_linear_calibrate_scales", "sfkv_linear_write", "sfkv_linear_workspace_bytes",
+    "sfkv_linear_attend", "sfkv_linear_state", "sfkv_linear_layout",
+    "sfkv_status_string", "sfkv_last_error",
 )
 
 
@@ -68,6 +76,15 @@ _sig("sfkv_attend", ctypes.c_int, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _
 _sig("sfkv_rebase_positions", ctypes.c_int, _vp, _i64, _vp)
 _sig("sfkv_cache_state", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i32), _P(_i32))
 _sig("sfkv_cache_layout", ctypes.c_int, _vp, _P(_sz), _P(_sz), _P(_sz), _P(_sz))
+_sig("sfkv_linear_bytes", _sz, _P(CacheConfig), ctypes.c_int)
+_sig("sfkv_linear_init", ctypes.c_int, _P(CacheConfig), _vp, ctypes.c_int, _vp, _sz, _vp, _P(_vp))
+_sig("sfkv_linear_destroy", None, _vp)
+_sig("sfkv_linear_calibrate_scales", ctypes.c_int, _vp, _vp, _vp, _i32, _vp)
+_sig("sfkv_linear_write", ctypes.c_int, _vp, _vp, _vp, _i32, _vp)
+_sig("sfkv_linear_workspace_bytes", _sz, _vp)
+_sig("sfkv_linear_attend", ctypes.c_int, _vp, _vp, _i32, _vp, _vp, _sz, _vp)
+_sig("sfkv_linear_state", ctypes.c_int, _vp, _P(_i32), _P(_i32))
+_sig("sfkv_linear_layout", ctypes.c_int, _vp, _P(_sz), _P(_sz), _P(_sz), _P(_sz))
 _sig("sfkv_status_string", ctypes.c_char_p, ctypes.c_int)
 _sig("sfkv_last_error", ctypes.c_char_p)
 
@@ -164,6 +181,46 @@ def cache_layout(handle: int) -> dict:
     return {"k": k.value, "v": v.value, "pos": p.value, "scales": s.value}
 
 
+def linear_bytes(cfg: CacheConfig, dtype: int) -> int:
+    return int(_lib.sfkv_linear_bytes(ctypes.byref(cfg), dtype))
+
+
+def linear_init(cfg: CacheConfig, rope_handle: int, dtype: int, buf: torch.Tensor, stream=None) -> int:
+    h = _vp()
+    _check(_lib.sfkv_linear_init(ctypes.byref(cfg), rope_handle, dtype, buf.data_ptr(), buf.numel(),
+                                 _stream(stream), ctypes.byref(h)))
+    return h.value
+
+
+def linear_calibrate_scales(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _check(_lib.sfkv_linear_calibrate_scales(handle, k.data_ptr(), v.data_ptr(), k.shape[0], _stream(stream)))
+
+
+def linear_write(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _check(_lib.sfkv_linear_write(handle, k.data_ptr(), v.data_ptr(), k.shape[0], _stream(stream)))
+
+
+def linear_workspace_bytes(handle: int) -> int:
+    return int(_lib.sfkv_linear_workspace_bytes(handle))
+
+
+def linear_attend(handle: int, q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor, stream=None):
+    _check(_lib.sfkv_linear_attend(handle, q.data_ptr(), q.shape[0], out.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def linear_state(handle: int) -> dict:
+    m, n = _i32(), _i32()
+    _check(_lib.sfkv_linear_state(handle, ctypes.byref(m), ctypes.byref(n)))
+    return {"n_window": m.value, "last_n": n.value}
+
+
+def linear_layout(handle: int) -> dict:
+    k, v, p, s = _sz(), _sz(), _sz(), _sz()
+    _check(_lib.sfkv_linear_layout(handle, ctypes.byref(k), ctypes.byref(v), ctypes.byref(p), ctypes.byref(s)))
+    return {"k": k.value, "v": v.value, "pos": p.value, "scales": s.value}
+
+
 # ---- owners -------------------------------------------------------------------
 class Rope:
     """RoPE table in a torch device buffer, shared by every cache of one head_dim."""
@@ -232,6 +289,77 @@ class RingCache:
         return cache_state(self.handle)
 
     # views into the device buffer (no copies)
+    def k_codes(self) -> torch.Tensor:
+        c = self.cfg
+        n = c.num_heads * c.capacity * c.head_dim
+        return self.buf[self.layout["k"]:self.layout["k"] + n].view(c.num_heads, c.capacity, c.head_dim)
+
+    def v_codes(self) -> torch.Tensor:
+        c = self.cfg
+        n = c.num_heads * c.capacity * c.head_dim
+        return self.buf[self.layout["v"]:self.layout["v"] + n].view(c.num_heads, c.capacity, c.head_dim)
+
+    def positions(self) -> torch.Tensor:
+        c = self.cfg
+        return self.buf[self.layout["pos"]:self.layout["pos"] + 4 * c.capacity].view(torch.int32)
+
+    def scales(self) -> torch.Tensor:
+        c = self.cfg
+        return self.buf[self.layout["scales"]:self.layout["scales"] + 16 * c.num_heads].view(torch.float32).view(4, c.num_heads)
+
+
+class LinearCache:
+    """The launch software's plain path: a copy-shifted raw window re-rotated and
+    re-quantised on every write (its device buffer, handle and views)."""
+
+    def __init__(self, rope: Rope, heads: int, capacity: int, max_new_tokens: Optional[int] = None,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", stream=None):
+        self.rope = rope
+        self.dtype = dtype
+        self.code = BF16 if dtype == torch.bfloat16 else FP32
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dtype must be bfloat16 or float32")
+        self.cfg = CacheConfig(heads, rope.head_dim, capacity, max_new_tokens or capacity)
+        n = linear_bytes(self.cfg, self.code)
+        if n == 0:
+            raise ValueError("invalid cache configuration")
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self._destroy = _lib.sfkv_linear_destroy    # still reachable at interpreter exit
+        self.handle = linear_init(self.cfg, rope.handle, self.code, self.buf, stream)
+        self.layout = linear_layout(self.handle)
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self._destroy(self.handle)
+            self.handle = None
+
+    def _in(self, t):
+        t = _frame(t, self.cfg.num_heads, self.cfg.head_dim)
+        if t.dtype != self.dtype:
+            raise TypeError(f"expected {self.dtype} inputs for this window")
+        return t
+
+    def calibrate_scales(self, k, v, stream=None):
+        linear_calibrate_scales(self.handle, self._in(k), self._in(v), stream)
+
+    def cache_write(self, k, v, stream=None):
+        linear_write(self.handle, self._in(k), self._in(v), stream)
+
+    def workspace_bytes(self) -> int:
+        return linear_workspace_bytes(self.handle)
+
+    def attend(self, q, out=None, workspace=None, stream=None):
+        q = self._in(q)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes(), dtype=torch.uint8, device=q.device)
+        linear_attend(self.handle, q, out, workspace, stream)
+        return out
+
+    def state(self) -> dict:
+        return linear_state(self.handle)
+
     def k_codes(self) -> torch.Tensor:
         c = self.cfg
         n = c.num_heads * c.capacity * c.head_dim

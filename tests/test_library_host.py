@@ -50,6 +50,18 @@ def test_buffer_sizes(sfkv):
     assert sfkv.rope_bytes(64, 1024) == 1025 * 32 * 8
 
 
+def test_linear_buffer_sizes(sfkv):
+    cfg = sfkv.CacheConfig(24, 128, 5788, 757)
+    planes = sfkv.cache_bytes(cfg)
+    window = 5788 * 24 * 128
+    for code, esize in ((sfkv.BF16, 2), (sfkv.FP32, 4)):
+        n = sfkv.linear_bytes(cfg, code)
+        assert n % 256 == 0
+        assert planes + 4 * window * esize <= n < planes + 4 * window * esize + 2 * 256
+    assert sfkv.linear_bytes(cfg, 7) == 0
+    assert sfkv.linear_bytes(sfkv.CacheConfig(1, 96, 64, 16), sfkv.BF16) == 0
+
+
 @pytest.mark.parametrize("cfg", [
     (0, 128, 64, 16), (1, 96, 64, 16), (1, 128, 0, 1), (1, 128, 64, 0), (1, 128, 64, 65),
     (4096, 128, 1 << 24, 16),     # a code plane of 2^43 bytes
@@ -86,6 +98,11 @@ def test_null_handles(sfkv):
     assert lib.sfkv_rebase_positions(None, 0, None) == sfkv.EINVAL
     assert lib.sfkv_cache_state(None, None, None, None, None) == sfkv.EINVAL
     assert lib.sfkv_attend_workspace_bytes(None) == 0
+    assert lib.sfkv_linear_write(None, 256, 256, 1, None) == sfkv.EINVAL
+    assert lib.sfkv_linear_calibrate_scales(None, 256, 256, 1, None) == sfkv.EINVAL
+    assert lib.sfkv_linear_attend(None, 256, 1, 256, None, 0, None) == sfkv.EINVAL
+    assert lib.sfkv_linear_state(None, None, None) == sfkv.EINVAL
+    assert lib.sfkv_linear_workspace_bytes(None) == 0
     assert lib.sfkv_status_string(-3) == b"position out of range"
 
 
