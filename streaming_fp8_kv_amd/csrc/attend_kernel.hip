@@ -286,9 +286,9 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
       pv[j] = uint2{w[0], w[1]};
     }
   };
-  // Staging of a loaded tile into LDS buffer buf, in three parts so that the
-  // pieces can sit between matrix instructions: K rows as they are, V widened
-  // to fp16 (exact) and stored transposed, one 8-byte column piece at a time.
+  // Staging of a loaded tile into LDS buffer buf, in parts so that the pieces
+  // can sit between matrix instructions: K rows as they are, V widened to fp16
+  // (exact: E4M3 is a subset of fp16), one 16-byte chunk of one key per store.
   auto store_k = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
