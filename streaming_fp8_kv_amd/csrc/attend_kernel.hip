@@ -222,15 +222,41 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   __shared__ __attribute__((aligned(16))) uint8_t sK[3][BK * KSTRIDE];
   __shared__ __attribute__((aligned(16))) _Float16 sV[3][BK * D];
 
+  // Work plan. Pair p = head * tiles_q + query tile is split along the keys
+  // into s_lo + 1 ranges when p < x ("small" workgroups) and s_lo otherwise
+  // ("big" ones). Workgroups are dealt to the 8 XCDs round-robin by block
+  // index, and inside an XCD the workgroup with local index j shares its CU
+  // with local index j + 32 (measured: the dispatcher fills every CU once
+  // before doubling up, in the same order). Each XCD therefore takes its share
+  // of the big workgroups at local indices 0.. and its share of the small ones
+  // after them, so that a big one is paired with a small one on every CU
+  // while big ones last. Consecutive workgroups of a share cover the splits
+  // and query tiles of the same heads, so a key range is fetched from HBM once
+  // into the XCD's L2 and read by every query tile of its head in step.
   const int tiles_q = (a.n_q + BQB - 1) / BQB;
-  const int n_blocks = tiles_q * a.heads * a.splits;
-  const int per_xcd = (n_blocks + 7) / 8;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (logical >= n_blocks) return;
-  const int qtile = logical % tiles_q;
-  const int group = logical / tiles_q;
-  const int h = group % a.heads;
-  const int split = group / a.heads;
+  const int n_pairs = tiles_q * a.heads;
+  const int NT = (a.n_valid + BK - 1) / BK;
+  const int slo = a.split_lo, X = a.split_x;
+  const int NB = (n_pairs - X) * slo, NS = X * (slo + 1);
+  const int xcd = blockIdx.x & 7, jl = blockIdx.x >> 3;
+  const int b0 = NB * xcd / 8, nb = NB * (xcd + 1) / 8 - b0;
+  const int s0 = NS * xcd / 8, ns = NS * (xcd + 1) / 8 - s0;
+  int pair, split, nsplit;
+  if (jl < nb) {
+    const int b = b0 + jl;
+    pair = X + b / slo;
+    split = b % slo;
+    nsplit = slo;
+  } else {
+    if (jl - nb >= ns) return;
+    const int sm = s0 + jl - nb;
+    pair = sm / (slo + 1);
+    split = sm % (slo + 1);
+    nsplit = slo + 1;
+  }
+  const int h = pair / tiles_q;
+  const int qtile = pair % tiles_q;
+  const int slot = pair * slo + min(pair, X) + split;   // partial slot of this range
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -242,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   int qscale[DH];
   load_query_terms<D>(a, h, qi, hh, qt, qscale);
 
-  const int per_split = ((a.n_valid + a.splits - 1) / a.splits + BK - 1) / BK * BK;
+  const int per_split = (NT + nsplit - 1) / nsplit * BK;
   const int kbeg = split * per_split;
   const int kend = min(a.n_valid, kbeg + per_split);
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
@@ -518,7 +544,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   l_run += l_run2;
   const float l_tot = l_run + other_half(l_run);
   if (qi >= a.n_q) return;
-  if (a.splits == 1) {
+  if (nsplit == 1) {
     const float f = a.scales[2 * H + h] / l_tot;
     float *o = a.out + (static_cast<size_t>(qi) * H + h) * D;
 #pragma unroll
@@ -529,7 +555,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
         *reinterpret_cast<float4 *>(o + 32 * db + 8 * j + 4 * hh) = v;
       }
   } else {
-    const size_t row = (static_cast<size_t>(split) * a.n_q + qi) * H + h;
+    const size_t row = static_cast<size_t>(slot) * BQB + wave * 32 + r;
     float *o = a.part_o + row * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -542,29 +568,37 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   }
 }
 
-// Merge split partials: one thread per 8 output dims of one (query, head) row.
-// NS > 0 fixes the split count at compile time so every load is issued at once.
+// Merge of the split partials: one thread per 8 output dims of one (query,
+// head) row; the row's pair has nsplit ranges in consecutive partial slots.
+// NS > 0 bounds the split count at compile time so every load is issued at
+// once; pairs with a single range were written directly.
 template <int D, int NS>
 __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
+  constexpr int BQB = kAttendQueriesPerBlock;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t rows = static_cast<size_t>(a.n_q) * a.heads;
   if (idx >= rows * (D / 8)) return;
   const size_t row = idx / (D / 8);
   const int c8 = static_cast<int>(idx % (D / 8));
   const int h = static_cast<int>(row % a.heads);
-  const int ns = NS > 0 ? NS : a.splits;
+  const int qi = static_cast<int>(row / a.heads);
+  const int tiles_q = (a.n_q + BQB - 1) / BQB;
+  const int pair = h * tiles_q + qi / BQB;
+  const int nsplit = a.split_lo + (pair < a.split_x ? 1 : 0);
+  if (nsplit == 1) return;
+  const size_t base = static_cast<size_t>(pair * a.split_lo + min(pair, a.split_x)) * BQB + qi % BQB;
   float mstar = kNegBig;
 #pragma unroll
-  for (int sp = 0; sp < (NS > 0 ? NS : 16); ++sp) {
-    if (NS == 0 && sp >= ns) break;
-    mstar = fmaxf(mstar, a.part_ml[2 * (sp * rows + row)]);
+  for (int sp = 0; sp < (NS > 0 ? NS : 64); ++sp) {
+    if (sp >= nsplit) break;
+    mstar = fmaxf(mstar, a.part_ml[2 * (base + static_cast<size_t>(sp) * BQB)]);
   }
   float L = 0.0f;
   float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int sp = 0; sp < (NS > 0 ? NS : 16); ++sp) {
-    if (NS == 0 && sp >= ns) break;
-    const size_t prow = sp * rows + row;
+  for (int sp = 0; sp < (NS > 0 ? NS : 64); ++sp) {
+    if (sp >= nsplit) break;
+    const size_t prow = base + static_cast<size_t>(sp) * BQB;
     const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * prow);
     const float w = __builtin_amdgcn_exp2f(ml.x - mstar);
     L += w * ml.y;
@@ -583,41 +617,48 @@ template <int D>
 void launch_combine(const AttendLaunch &a, hipStream_t st) {
   const size_t threads = static_cast<size_t>(a.n_q) * a.heads * (D / 8);
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-  switch (a.splits) {
-    case 2: hipLaunchKernelGGL((combine_kernel<D, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((combine_kernel<D, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((combine_kernel<D, 0>), grid, dim3(256), 0, st, a); break;
-  }
+  const int most = a.split_lo + (a.split_x > 0 ? 1 : 0);
+  if (most <= 2) hipLaunchKernelGGL((combine_kernel<D, 2>), grid, dim3(256), 0, st, a);
+  else if (most <= 4) hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, st, a);
+  else if (most <= 8) hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((combine_kernel<D, 0>), grid, dim3(256), 0, st, a);
 }
 
 }  // namespace
 
-int attend_splits(int n_q, int heads, int capacity) {
-  // about two workgroups per CU, each with at least four key tiles
-  const int tiles = (n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock;
-  const int blocks = tiles * heads;
-  int s = (2 * 256) / blocks;
-  if (const char *env = getenv("SFKV_ATTEND_SPLITS")) s = atoi(env);
-  const int max_by_keys = capacity / (4 * BK);
-  if (s > max_by_keys) s = max_by_keys;
-  if (s > 16) s = 16;
-  return s < 1 ? 1 : s;
+AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus) {
+  // about two workgroups per CU, each key range at least four tiles long
+  const int64_t pairs = static_cast<int64_t>((n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock) * heads;
+  const int64_t nt = (n_valid + BK - 1) / BK;
+  const int64_t max_split = nt / 4 > 1 ? nt / 4 : 1;
+  int64_t g = 2 * static_cast<int64_t>(cus > 0 ? cus : 256);
+  if (const char *env = getenv("SFKV_ATTEND_WORKERS")) g = atoi(env);
+  if (g > pairs * max_split) g = pairs * max_split;
+  if (g < pairs) g = pairs;
+  AttendPlan p;
+  p.s_lo = static_cast<int>(g / pairs);
+  p.x = static_cast<int>(g % pairs);
+  p.workers = static_cast<int>(pairs * p.s_lo + p.x);
+  return p;
 }
 
 hipError_t launch_attend(const AttendLaunch &a, hipStream_t st) {
-  const int n_blocks = (a.n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock * a.heads * a.splits;
-  const dim3 grid((n_blocks + 7) / 8 * 8);
+  const int tiles_q = (a.n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock;
+  const int n_pairs = tiles_q * a.heads;
+  const int NB = (n_pairs - a.split_x) * a.split_lo, NS = a.split_x * (a.split_lo + 1);
+  const int per_xcd = (NB + 7) / 8 + (NS + 7) / 8;   // largest XCD share
+  const dim3 grid(8 * per_xcd);
   const unsigned prep_threads = static_cast<unsigned>(a.n_q) * a.heads * (a.head_dim / 8);
   const dim3 prep_grid((prep_threads + 255) / 256);
+  const bool merge = a.split_lo > 1 || a.split_x > 0;
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(query_prep_kernel<128>, prep_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(256), 0, st, a);
-    if (a.splits > 1) launch_combine<128>(a, st);
+    if (merge) launch_combine<128>(a, st);
   } else {
     hipLaunchKernelGGL(query_prep_kernel<64>, prep_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(256), 0, st, a);
-    if (a.splits > 1) launch_combine<64>(a, st);
+    if (merge) launch_combine<64>(a, st);
   }
   return hipGetLastError();
 }

@@ -31,6 +31,7 @@ struct sfkv_cache {
   int64_t next_pos;
   int64_t last_pos0;
   int32_t last_n;
+  int cus;          // compute units of the device the cache was set up on
   bool calibrated;
 };
 
@@ -93,6 +94,15 @@ sfkv_status check_frame(const sfkv_cache *c, const void *k, const void *v, sfkv_
   if (c->next_pos + n > c->rope->max_position)
     return fail(SFKV_ERANGE, "positions of this frame would reach max_position");
   return SFKV_OK;
+}
+
+// Compute units of the current device (the attention grid is planned for two
+// workgroups per CU); 256 if the runtime cannot say.
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
+  return cus;
 }
 
 sfkv_status launched(hipError_t e) {
@@ -193,6 +203,7 @@ sfkv_status sfkv_cache_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, vo
   c->next_pos = 0;
   c->last_pos0 = 0;
   c->last_n = 0;
+  c->cus = device_cus();
   c->calibrated = false;
   *out = c;
   return ok();
@@ -252,51 +263,51 @@ static int n_valid_of(const sfkv_cache *c) {
   return static_cast<int>(c->tokens < c->cfg.capacity ? c->tokens : c->cfg.capacity);
 }
 
-// Attend workspace, sized once per cache for its largest write (a call with
-// fewer queries caps its split count to fit, so one buffer serves every token
-// count):
+// Attend workspace, sized once per cache configuration for its largest write
+// and the device's CU count (a call with fewer queries or valid slots plans
+// fewer or equal workgroups, so one buffer serves every token count):
 //   query terms   [max_new][heads][3][head_dim] bytes
 //   query scales  [max_new][heads][head_dim/32] words
-//   split partials: O rows [splits][n_q][heads][head_dim] fp32, then (max, sum)
+//   split partials: O rows [workers][128][head_dim] fp32, then (max, sum)
 struct AttendWs {
-  size_t qterm, qscale, part_o, part_ml, total, rows_cap;
+  size_t qterm, qscale, part_o, part_ml, total, slots;
 };
 
-static AttendWs attend_ws(const sfkv_cache_cfg &cfg) {
+static AttendWs attend_ws(const sfkv_cache_cfg &cfg, int cus) {
   AttendWs w;
   const size_t qh = static_cast<size_t>(cfg.max_new_tokens) * cfg.num_heads;
-  const int s = sfkv::attend_splits(cfg.max_new_tokens, cfg.num_heads, cfg.capacity);
-  w.rows_cap = s > 1 ? static_cast<size_t>(s) * qh : 0;
+  w.slots = static_cast<size_t>(sfkv::attend_plan(cfg.max_new_tokens, cfg.num_heads, cfg.capacity, cus).workers);
+  const size_t rows = w.slots * sfkv::kAttendQueriesPerBlock;
   w.qterm = 0;
   w.qscale = align_up(qh * 3 * cfg.head_dim, 256);
   w.part_o = align_up(w.qscale + qh * (cfg.head_dim / 32) * sizeof(uint32_t), 256);
-  w.part_ml = align_up(w.part_o + w.rows_cap * cfg.head_dim * sizeof(float), 256);
-  w.total = align_up(w.part_ml + w.rows_cap * 2 * sizeof(float), 256);
+  w.part_ml = align_up(w.part_o + rows * cfg.head_dim * sizeof(float), 256);
+  w.total = align_up(w.part_ml + rows * 2 * sizeof(float), 256);
   return w;
 }
 
 size_t sfkv_attend_workspace_bytes(const sfkv_cache *c) {
   if (!c) return 0;
-  return attend_ws(c->cfg).total;
+  return attend_ws(c->cfg, c->cus).total;
 }
 
 // One attend launch over FP8 planes laid out as layout_of(cfg) at `base`:
 // n_valid slots, queries at positions qpos0 .. qpos0 + n_q - 1.
-static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, const sfkv_rope *rope, uint8_t *base,
+static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_rope *rope, uint8_t *base,
                                  int nv, int64_t qpos0, const void *q, sfkv_dtype dtype, int32_t n_q,
                                  float *out, void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !out) return fail(SFKV_EINVAL, "q and out must be device pointers");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(SFKV_EINVAL, "q and out must be 16-byte aligned");
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
-  const AttendWs ws = attend_ws(cfg);
+  const AttendWs ws = attend_ws(cfg, cus);
   if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 256))
     return fail(SFKV_EINVAL, "workspace missing, smaller than the attend workspace size or not 256-byte aligned");
   const Layout l = layout_of(cfg);
-  const size_t rows_per_split = static_cast<size_t>(n_q) * cfg.num_heads;
-  int splits = sfkv::attend_splits(n_q, cfg.num_heads, nv);
-  if (splits > 1 && static_cast<size_t>(splits) * rows_per_split > ws.rows_cap)
-    splits = static_cast<int>(ws.rows_cap / rows_per_split);
-  if (splits < 2) splits = 1;
+  // n_q <= max_new and nv <= capacity, so the plan never needs more partial
+  // slots than the workspace holds; checked anyway
+  const sfkv::AttendPlan plan = sfkv::attend_plan(n_q, cfg.num_heads, nv, cus);
+  if (static_cast<size_t>(plan.workers) > ws.slots)
+    return fail(SFKV_EINVAL, "attend plan exceeds the workspace (n_q or n_valid above the configured sizes)");
   sfkv::AttendLaunch a;
   a.q = q;
   a.dtype = dtype;
@@ -311,12 +322,14 @@ static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, const sfkv_rope *rop
   a.v8 = base + l.v;
   a.scales = reinterpret_cast<const float *>(base + l.scale);
   a.out = out;
-  a.splits = splits;
+  a.workers = plan.workers;
+  a.split_lo = plan.s_lo;
+  a.split_x = plan.x;
   uint8_t *wsb = static_cast<uint8_t *>(workspace);
   a.qterm = wsb + ws.qterm;
   a.qscale = reinterpret_cast<uint32_t *>(wsb + ws.qscale);
-  a.part_o = splits > 1 ? reinterpret_cast<float *>(wsb + ws.part_o) : nullptr;
-  a.part_ml = splits > 1 ? reinterpret_cast<float *>(wsb + ws.part_ml) : nullptr;
+  a.part_o = reinterpret_cast<float *>(wsb + ws.part_o);
+  a.part_ml = reinterpret_cast<float *>(wsb + ws.part_ml);
   return launched(sfkv::launch_attend(a, as_stream(stream)));
 }
 
@@ -325,7 +338,7 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   if (!c) return fail(SFKV_EINVAL, "cache is NULL");
   if (c->last_n == 0) return fail(SFKV_ESTATE, "attend before any cache_write");
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
-  return attend_planes(c->cfg, c->rope, c->base, n_valid_of(c), c->last_pos0, q, dtype, n_q, out,
+  return attend_planes(c->cfg, c->cus, c->rope, c->base, n_valid_of(c), c->last_pos0, q, dtype, n_q, out,
                        workspace, workspace_bytes, stream);
 }
 
@@ -390,6 +403,7 @@ struct sfkv_linear {
   int32_t m;             // tokens in the window
   int32_t last_n;
   int cur;               // window holding the current tokens
+  int cus;               // compute units of the device the cache was set up on
   bool calibrated;
 };
 
@@ -457,6 +471,7 @@ sfkv_status sfkv_linear_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, s
   c->m = 0;
   c->last_n = 0;
   c->cur = 0;
+  c->cus = device_cus();
   c->calibrated = false;
   *out = c;
   return ok();
@@ -533,7 +548,7 @@ sfkv_status sfkv_linear_write(sfkv_linear *c, const void *k, const void *v, int3
 
 size_t sfkv_linear_workspace_bytes(const sfkv_linear *c) {
   if (!c) return 0;
-  return attend_ws(c->cfg).total;
+  return attend_ws(c->cfg, c->cus).total;
 }
 
 sfkv_status sfkv_linear_attend(sfkv_linear *c, const void *q, int32_t n_q, float *out, void *workspace,
@@ -541,7 +556,7 @@ sfkv_status sfkv_linear_attend(sfkv_linear *c, const void *q, int32_t n_q, float
   if (!c) return fail(SFKV_EINVAL, "linear cache is NULL");
   if (c->last_n == 0) return fail(SFKV_ESTATE, "linear_attend before any linear_write");
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last linear_write");
-  return attend_planes(c->cfg, c->rope, c->base, c->m, c->m - c->last_n, q, c->dtype, n_q, out,
+  return attend_planes(c->cfg, c->cus, c->rope, c->base, c->m, c->m - c->last_n, q, c->dtype, n_q, out,
                        workspace, workspace_bytes, stream);
 }
 

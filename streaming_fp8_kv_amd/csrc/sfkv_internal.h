@@ -46,9 +46,10 @@ struct AttendLaunch {
   const uint8_t *k8, *v8;
   const float *scales;
   float *out;
-  int splits;                // key-range splits; 1 writes `out` directly
-  float *part_o;             // [splits][n_q][heads][head_dim] when splits > 1
-  float *part_ml;            // [splits][n_q][heads][2]
+  int workers;               // attention workgroups (see AttendPlan)
+  int split_lo, split_x;     // the plan's s_lo and x
+  float *part_o;             // [workers][128 rows][head_dim] split partials
+  float *part_ml;            // [workers][128 rows][2] (max, sum)
   uint8_t *qterm;            // [n_q][heads][3][head_dim] E4M3 query terms
   uint32_t *qscale;          // [n_q][heads][head_dim/32] E8M0 scales, byte t = term t
 };
@@ -73,6 +74,14 @@ hipError_t launch_attend(const AttendLaunch &a, hipStream_t s);
 // Attention tiling shared by the launcher and the workspace sizing.
 constexpr int kAttendQueriesPerBlock = 128;  // 4 waves x 32 queries
 constexpr int kAttendKeysPerTile = 64;
-int attend_splits(int n_q, int heads, int capacity);
+// Work plan of one attend launch. The (head, 128-query tile) pairs are split
+// along the keys: the first `x` pairs into s_lo + 1 ranges ("small" ranges),
+// the others into s_lo ("big" ranges), so there are exactly
+// workers = pairs * s_lo + x workgroups, ideally two per CU. Big workgroups
+// are placed where each one shares its CU with a small one.
+struct AttendPlan {
+  int workers, s_lo, x;
+};
+AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus);
 
 }  // namespace sfkv
