@@ -571,7 +571,8 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 // Merge of the split partials: one thread per 8 output dims of one (query,
 // head) row; the row's pair has nsplit ranges in consecutive partial slots.
 // NS > 0 bounds the split count at compile time so every load is issued at
-// once; pairs with a single range were written directly.
+// once (slots past nsplit re-read slot 0 and get weight 0); pairs with a single
+// range were written directly.
 template <int D, int NS>
 __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
   constexpr int BQB = kAttendQueriesPerBlock;
@@ -587,25 +588,45 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
   const int nsplit = a.split_lo + (pair < a.split_x ? 1 : 0);
   if (nsplit == 1) return;
   const size_t base = static_cast<size_t>(pair * a.split_lo + min(pair, a.split_x)) * BQB + qi % BQB;
-  float mstar = kNegBig;
-#pragma unroll
-  for (int sp = 0; sp < (NS > 0 ? NS : 64); ++sp) {
-    if (sp >= nsplit) break;
-    mstar = fmaxf(mstar, a.part_ml[2 * (base + static_cast<size_t>(sp) * BQB)]);
-  }
   float L = 0.0f;
   float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  if (NS > 0) {
+    // every partial of the row is loaded before any arithmetic
+    float2 ml[NS > 0 ? NS : 1];
+    float4 o0[NS > 0 ? NS : 1], o1[NS > 0 ? NS : 1];
 #pragma unroll
-  for (int sp = 0; sp < (NS > 0 ? NS : 64); ++sp) {
-    if (sp >= nsplit) break;
-    const size_t prow = base + static_cast<size_t>(sp) * BQB;
-    const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * prow);
-    const float w = __builtin_amdgcn_exp2f(ml.x - mstar);
-    L += w * ml.y;
-    const float4 *o = reinterpret_cast<const float4 *>(a.part_o + prow * D + 8 * c8);
-    const float4 o0 = o[0], o1 = o[1];
-    acc[0] += w * o0.x; acc[1] += w * o0.y; acc[2] += w * o0.z; acc[3] += w * o0.w;
-    acc[4] += w * o1.x; acc[5] += w * o1.y; acc[6] += w * o1.z; acc[7] += w * o1.w;
+    for (int sp = 0; sp < NS; ++sp) {
+      const size_t prow = base + static_cast<size_t>(sp < nsplit ? sp : 0) * BQB;
+      ml[sp] = *reinterpret_cast<const float2 *>(a.part_ml + 2 * prow);
+      const float4 *o = reinterpret_cast<const float4 *>(a.part_o + prow * D + 8 * c8);
+      o0[sp] = o[0];
+      o1[sp] = o[1];
+    }
+    float mstar = kNegBig;
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+      if (sp < nsplit) mstar = fmaxf(mstar, ml[sp].x);
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) {
+      const float w = sp < nsplit ? __builtin_amdgcn_exp2f(ml[sp].x - mstar) : 0.0f;
+      L += w * ml[sp].y;
+      acc[0] += w * o0[sp].x; acc[1] += w * o0[sp].y; acc[2] += w * o0[sp].z; acc[3] += w * o0[sp].w;
+      acc[4] += w * o1[sp].x; acc[5] += w * o1[sp].y; acc[6] += w * o1[sp].z; acc[7] += w * o1[sp].w;
+    }
+  } else {
+    float mstar = kNegBig;
+    for (int sp = 0; sp < nsplit; ++sp)
+      mstar = fmaxf(mstar, a.part_ml[2 * (base + static_cast<size_t>(sp) * BQB)]);
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const size_t prow = base + static_cast<size_t>(sp) * BQB;
+      const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * prow);
+      const float w = __builtin_amdgcn_exp2f(ml.x - mstar);
+      L += w * ml.y;
+      const float4 *o = reinterpret_cast<const float4 *>(a.part_o + prow * D + 8 * c8);
+      const float4 p0 = o[0], p1 = o[1];
+      acc[0] += w * p0.x; acc[1] += w * p0.y; acc[2] += w * p0.z; acc[3] += w * p0.w;
+      acc[4] += w * p1.x; acc[5] += w * p1.y; acc[6] += w * p1.z; acc[7] += w * p1.w;
+    }
   }
   const float f = a.scales[2 * a.heads + h] / L;
   float4 *dst = reinterpret_cast<float4 *>(a.out + row * D + 8 * c8);

@@ -169,3 +169,31 @@ def test_sweep_launch_configuration(sfkv):
         a, b = attention_error(got, ref)
         say(f"  cache {ci}: A={a:.2e} B={b:.2e}")
         assert a <= A_MAX and b <= B_MEAN
+
+
+@pytest.mark.parametrize("heads,d,cap,max_new,lens", [
+    (3, 128, 1000, 1000, [1000, 1, 37, 999]),   # a write that fills the whole ring, then ragged ones
+    (5, 128, 333, 64, [1, 1, 64, 63, 64, 64, 64, 64, 2]),   # capacity not a multiple of the key tile
+    (2, 64, 4096, 700, [700, 129, 700, 700, 700, 700, 700]),   # head_dim 64 at a long ring, wrapped
+    (1, 128, 64, 64, [64, 64, 64]),             # a single key tile, fully replaced each write
+])
+def test_ragged_shapes(sfkv, heads, d, cap, max_new, lens):
+    """Shapes off the production grid: a single-token write, a whole-ring write,
+    capacities and token counts that are not multiples of the 64-key tile or the
+    32-query block, head_dim 64, and every call checked in full."""
+    say(f"case ragged_h{heads}_d{d}_c{cap}_max{max_new}")
+    shape = W.CacheShape(heads, d, cap, max_new, max_position=16384)
+    spec = W.WorkloadSpec(name="ragged", shape=shape, seed=11 + heads, dtype=torch.bfloat16, dist="normal",
+                          sigma_q=(0.5, 4.0), sigma_kv=(0.5, 4.0), steps=len(lens))
+    m = Mirror(sfkv, rope_for(sfkv, shape), spec)
+    fs = W.FrameStream(spec)
+    for step, n in enumerate(lens):
+        q, k, v = fs.frame(n)
+        if step == 0:
+            m.calibrate(k, v)
+        if step == len(lens) // 2:
+            m.rebase(7)
+            m.check_cache(f"step {step} after rebase")
+        m.write(k, v)
+        m.check_cache(f"step {step}")
+        m.check_attend(q, tag=f"step {step} n={n}")
