@@ -15,6 +15,8 @@ here as the plain semantics the ring must reproduce).
 
 Modules:
   e4m3       OCP E4M3FN encode (clamp, round-to-nearest-even) and decode
+  bf16       bfloat16 encode (round-to-nearest-even) and decode, for the
+             non-FP8 ring variant
   rope       RoPE table (fp64 libm, rounded to fp32) and pair rotation
   cache      the ring cache: calibrate, write, attend, rebase
   reference  plain definitions the ring is pinned against: direct softmax

@@ -20,10 +20,17 @@ Readings where the pages are silent (each listed in the design notes):
   * a rebase rotates the stored FP8 codes by -delta in the code domain (the
     per-head scale cancels, since rotation is linear), clamps and re-encodes.
 
-Two modes:
+Three modes:
   ``fp8``  the bit-exact pipeline: fp32 rotation without fused multiply-add,
            one fp32 multiply by the inverse scale, clamp, round-to-nearest-even
            E4M3; attention then in fp64 on the decoded cache.
+  ``bf16`` the non-FP8 variant ("Blackwell and Beyond Four GPUs" weighs the
+           FP8 cache against one without FP8): the same fp32 rotation, then
+           keys and values rounded to bfloat16 (nearest, ties to even); no
+           quantisation scale enters the values. Calibration records one
+           power-of-two factor per head and tensor (2^e with the absmax in
+           [256, 512) * 2^e), which the GPU uses to move bf16 values into
+           fp16 range exactly; attention is in fp64 on the bf16 values.
   ``fp64`` the same ring with exact arithmetic and no quantisation, used to pin
            the ring against the plain linear definition.
 
@@ -38,15 +45,15 @@ from typing import Optional
 
 import numpy as np
 
-from . import e4m3, rope
+from . import bf16, e4m3, rope
 
 
 class RingCache:
     def __init__(self, heads: int, head_dim: int, capacity: int,
                  max_new_tokens: Optional[int] = None, rope_base: float = 10000.0,
                  max_position: int = 65536, mode: str = "fp8"):
-        if mode not in ("fp8", "fp64"):
-            raise ValueError("mode must be 'fp8' or 'fp64'")
+        if mode not in ("fp8", "bf16", "fp64"):
+            raise ValueError("mode must be 'fp8', 'bf16' or 'fp64'")
         if head_dim % 2:
             raise ValueError("head_dim must be even")
         self.H, self.d, self.C = int(heads), int(head_dim), int(capacity)
@@ -59,6 +66,9 @@ class RingCache:
         if mode == "fp8":
             self.k = np.zeros((self.H, self.C, self.d), dtype=np.uint8)
             self.v = np.zeros((self.H, self.C, self.d), dtype=np.uint8)
+        elif mode == "bf16":
+            self.k = np.zeros((self.H, self.C, self.d), dtype=np.uint16)
+            self.v = np.zeros((self.H, self.C, self.d), dtype=np.uint16)
         else:
             self.k = np.zeros((self.H, self.C, self.d), dtype=np.float64)
             self.v = np.zeros((self.H, self.C, self.d), dtype=np.float64)
@@ -93,6 +103,15 @@ class RingCache:
             return np.float32(1.0), np.float32(1.0)
         return np.float32(float(m) / 448.0), np.float32(448.0 / float(m))
 
+    @staticmethod
+    def _pow2_pair(m: float):
+        """bf16 mode: (2^e, 2^-e) with m * 2^-e in [256, 512); (1, 1) for m = 0."""
+        if m == 0.0:
+            return np.float32(1.0), np.float32(1.0)
+        _, ex = math.frexp(float(m))          # m = f * 2^ex, f in [0.5, 1)
+        e = min(max(ex - 9, -126), 127)
+        return np.float32(math.ldexp(1.0, e)), np.float32(math.ldexp(1.0, -e))
+
     def calibrate(self, k, v):
         """Per-head scales from one frame ``[n, H, d]`` at the next write's positions."""
         k = np.asarray(k, dtype=np.float32)
@@ -105,11 +124,12 @@ class RingCache:
         kr = rope.rotate(k, c[:, None, :], s[:, None, :])
         mk = np.abs(kr).max(axis=(0, 2))
         mv = np.abs(v).max(axis=(0, 2))
+        pair = self._pow2_pair if self.mode == "bf16" else self._scale_pair
         sk, ik, sv, iv = [], [], [], []
         for h in range(self.H):
-            a, b = self._scale_pair(float(mk[h]))
+            a, b = pair(float(mk[h]))
             sk.append(a); ik.append(b)
-            a, b = self._scale_pair(float(mv[h]))
+            a, b = pair(float(mv[h]))
             sv.append(a); iv.append(b)
         self.scale_k = np.array(sk, dtype=np.float32)
         self.inv_k = np.array(ik, dtype=np.float32)
@@ -150,6 +170,13 @@ class RingCache:
             v8 = e4m3.quantize(v, self.inv_v[None, :, None])
             self.k[:, slots, :] = np.transpose(k8, (1, 0, 2))
             self.v[:, slots, :] = np.transpose(v8, (1, 0, 2))
+        elif self.mode == "bf16":
+            if self.inv_k is None:
+                raise RuntimeError("write before calibrate")
+            c, s = rope.cos_sin(pos, self.d, self.base)
+            kr = rope.rotate(k, c[:, None, :], s[:, None, :])
+            self.k[:, slots, :] = np.transpose(bf16.encode(kr), (1, 0, 2))
+            self.v[:, slots, :] = np.transpose(bf16.encode(v), (1, 0, 2))
         else:
             kr = rope.rotate64(k.astype(np.float64), pos, self.d, self.base)
             self.k[:, slots, :] = np.transpose(kr, (1, 0, 2))
@@ -166,19 +193,22 @@ class RingCache:
         if self.mode == "fp8":
             kk = e4m3.decode(self.k[:, :nv, :]) * self.scale_k.astype(np.float64)[:, None, None]
             vv = e4m3.decode(self.v[:, :nv, :]) * self.scale_v.astype(np.float64)[:, None, None]
+        elif self.mode == "bf16":
+            kk = bf16.decode(self.k[:, :nv, :]).astype(np.float64)
+            vv = bf16.decode(self.v[:, :nv, :]).astype(np.float64)
         else:
             kk, vv = self.k[:, :nv, :], self.v[:, :nv, :]
         return kk, vv
 
     def rotated_queries(self, q) -> np.ndarray:
-        """The last write's queries rotated at its positions (fp32 in fp8 mode)."""
+        """The last write's queries rotated at its positions (fp32 in fp8 and bf16 modes)."""
         q = np.asarray(q, dtype=np.float32)
         if self.last_pos0 is None:
             raise RuntimeError("attend before any write")
         if q.ndim != 3 or q.shape != (self.last_n, self.H, self.d):
             raise ValueError("queries must be the last write's [n, heads, head_dim]")
         pos = self.last_pos0 + np.arange(self.last_n, dtype=np.int64)
-        if self.mode == "fp8":
+        if self.mode in ("fp8", "bf16"):
             c, s = rope.cos_sin(pos, self.d, self.base)
             return rope.rotate(q, c[:, None, :], s[:, None, :]).astype(np.float64)
         return rope.rotate64(q.astype(np.float64), pos, self.d, self.base)
@@ -207,6 +237,10 @@ class RingCache:
             x = e4m3.decode(self.k[:, :nv, :]).astype(np.float32)          # exact
             y = rope.rotate_back(x, c[0], s[0])
             self.k[:, :nv, :] = e4m3.encode(y)
+        elif self.mode == "bf16":
+            c, s = rope.cos_sin([delta], self.d, self.base)
+            x = bf16.decode(self.k[:, :nv, :])                                 # exact
+            self.k[:, :nv, :] = bf16.encode(rope.rotate_back(x, c[0], s[0]))
         else:
             pos = np.full(nv, -delta, dtype=np.int64)
             kt = np.transpose(self.k[:, :nv, :], (1, 0, 2))                 # [nv, H, d]
