@@ -69,12 +69,25 @@ typedef enum {
 
 typedef enum { SFKV_BF16 = 0, SFKV_FP32 = 1 } sfkv_dtype;
 
+/* Element storage of the cached keys and values.
+ * SFKV_STORE_E4M3: one OCP E4M3 byte per element with per-head fp32 scales
+ *   ("Halving the Cache": FP8 with per-head scales).
+ * SFKV_STORE_BF16: two bytes per element, the rotated key and the value each
+ *   rounded once to bfloat16 (round to nearest even), no quantisation scale
+ *   ("Blackwell and Beyond Four GPUs" weighs the FP8 cache against one without
+ *   FP8). Its scale slots hold one power-of-two factor per head and tensor,
+ *   2^e with the calibration frame's absmax in [256, 512) * 2^e, by which the
+ *   attention moves bf16 values into fp16 exactly. */
+typedef enum { SFKV_STORE_E4M3 = 0, SFKV_STORE_BF16 = 1 } sfkv_storage;
+
 typedef struct {
   int32_t num_heads;      /* >= 1 */
   int32_t head_dim;       /* 64 or 128 */
   int32_t capacity;       /* ring slots, >= 1 */
   int32_t max_new_tokens; /* largest n_tokens of one write, in [1, capacity] */
-  /* num_heads * capacity * head_dim must be below 2^31 (one code plane < 2 GiB) */
+  int32_t storage;        /* sfkv_storage; 0 (E4M3) when zero-initialised */
+  /* one plane, num_heads * capacity * head_dim elements of the storage's
+   * size, must be below 2^31 bytes */
 } sfkv_cache_cfg;
 
 /* ---- RoPE table ---------------------------------------------------------

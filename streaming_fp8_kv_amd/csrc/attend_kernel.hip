@@ -47,6 +47,8 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int BK = kAttendKeysPerTile;      // 64 keys per LDS tile
 constexpr int KSTRIDE = 144;                // bytes per key row in LDS (128 + 16 pad)
@@ -190,6 +192,60 @@ __device__ inline void load_query_terms(const AttendLaunch &a, int h, int qi, in
   }
 }
 
+// Query preparation for a bfloat16 cache, once per call: RoPE at the query's
+// position, times log2(e) / sqrt(d) (the keys are used as stored, unscaled),
+// then two bf16 terms q = hi + lo with lo the rounding of what hi left over,
+// about 16 significant bits. Stored [query][head][term][dim] as bf16; one
+// thread per 8 dims.
+template <int D>
+__global__ __launch_bounds__(256) void query_prep_bf16_kernel(AttendLaunch a) {
+  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<unsigned>(a.n_q) * a.heads * (D / 8)) return;
+  const int g8 = idx % (D / 8);
+  const unsigned qh = idx / (D / 8);
+  const int qi = qh / a.heads;
+  float x[8];
+  load8(a.q, static_cast<size_t>(qh) * D + 8 * g8, a.dtype, x);
+  const int qp = a.qpos0 + qi;
+  const float sgn = qp < 0 ? -1.0f : 1.0f;
+  const RopePair *row = a.rope + static_cast<size_t>(qp < 0 ? -qp : qp) * (D / 2) + 4 * g8;
+  const float qs = kLog2e * (1.0f / sqrtf(static_cast<float>(D)));
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    RopePair cs = row[j];
+    cs.s *= sgn;
+    const float u = x[2 * j], v = x[2 * j + 1];
+    const float a0 = (u * cs.c - v * cs.s) * qs, a1 = (u * cs.s + v * cs.c) * qs;
+    const v2bf h = __builtin_convertvector((float2_t){a0, a1}, v2bf);
+    const float r0 = a0 - static_cast<float>(h[0]), r1 = a1 - static_cast<float>(h[1]);
+    hi[j] = __builtin_bit_cast(uint32_t, h);
+    lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){r0, r1}, v2bf));
+  }
+  uint4 *dst = reinterpret_cast<uint4 *>(a.qterm + (static_cast<size_t>(qh) * 2 * D + 8 * g8) * 2);
+  dst[0] = uint4{hi[0], hi[1], hi[2], hi[3]};
+  dst[D / 8] = uint4{lo[0], lo[1], lo[2], lo[3]};
+}
+
+// bf16 query terms of one lane for every 16-dim step ks: dims 16 ks + 8 hh ..
+// + 7 of query column qi (the B operand of the bf16 MFMA 32x32x16). Rows past
+// n_q load as zeros.
+template <int D>
+__device__ inline void load_query_terms_bf16(const AttendLaunch &a, int h, int qi, int hh, v8bf qb[2][D / 16]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qb[t][ks] = __builtin_bit_cast(v8bf, uint4{0, 0, 0, 0});
+  if (qi >= a.n_q) return;
+  const size_t qh = static_cast<size_t>(qi) * a.heads + h;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qb[t][ks] = __builtin_bit_cast(
+          v8bf, *reinterpret_cast<const uint4 *>(a.qterm + ((qh * 2 + t) * D + 16 * ks + 8 * hh) * 2));
+}
+
 // A pointer the compiler can keep in scalar registers.
 __device__ __forceinline__ void *uniform_ptr(const void *p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -213,13 +269,23 @@ __device__ __forceinline__ float other_half(float x) {
 // loaded into registers meanwhile. The grid is one-dimensional and remapped so
 // that all query tiles of one (head, key range) run on the same XCD and share
 // its L2 (workgroups are dealt to the 8 XCDs round-robin).
-template <int D>
-__global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
+//
+// ST selects the cache storage. kE4M3: raw E4M3 keys into the block-scaled FP8
+// MFMA with three query terms, two workgroups per CU. kBF16 (the non-FP8
+// variant): bf16 keys as stored into the bf16 MFMA 32x32x16 with two query
+// terms, and bf16 values moved into fp16 by the head's power-of-two factor;
+// a bf16 key tile is twice the size, so the three buffers leave room for one
+// workgroup per CU.
+template <int D, int ST>
+__global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(AttendLaunch a) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  constexpr bool BF = ST == kBF16;
+  constexpr int ES = BF ? 2 : 1;      // bytes per stored element
   constexpr int DH = D / 64;          // 64-dim halves of the head
   constexpr int BQB = 128;            // queries per workgroup
   constexpr float kShiftAt = 15.0f;   // P = exp2(s - m_ref) stays <= 2^15, inside fp16
-  __shared__ __attribute__((aligned(16))) uint8_t sK[3][BK * KSTRIDE];
+  constexpr int KROW = BF ? 2 * D + 16 : KSTRIDE;   // bytes per key row in LDS
+  __shared__ __attribute__((aligned(16))) uint8_t sK[3][BK * KROW];
   __shared__ __attribute__((aligned(16))) _Float16 sV[3][BK * D];
 
   // Work plan. Pair p = head * tiles_q + query tile is split along the keys
@@ -266,27 +332,31 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 
   v8i qt[DH][3];
   int qscale[DH];
-  load_query_terms<D>(a, h, qi, hh, qt, qscale);
+  v8bf qb[2][D / 16];
+  if constexpr (BF) load_query_terms_bf16<D>(a, h, qi, hh, qb);
+  else load_query_terms<D>(a, h, qi, hh, qt, qscale);
 
   const int per_split = (NT + nsplit - 1) / nsplit * BK;
   const int kbeg = split * per_split;
   const int kend = min(a.n_valid, kbeg + per_split);
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  const uint8_t *kplane = a.k8 + static_cast<size_t>(h) * a.capacity * D;
-  const uint8_t *vplane = a.v8 + static_cast<size_t>(h) * a.capacity * D;
+  const uint8_t *kplane = a.k8 + static_cast<size_t>(h) * a.capacity * D * ES;
+  const uint8_t *vplane = a.v8 + static_cast<size_t>(h) * a.capacity * D * ES;
 
   // staging roles: K = 16-byte chunks (D/16 per row); V = 4 keys x 8 dims, the
   // 16 lanes of a row group reading one 128-byte row together. Loads go through
   // buffer descriptors whose size ends at this workgroup's last key, so rows
   // past the range read as zeros without touching memory; the per-thread offset
   // is fixed and the tile start is the scalar offset.
-  constexpr int KPASS = (BK * D / 16) / 256;
+  constexpr int KPASS = (BK * D * ES / 16) / 256;
+  constexpr int KCH = D * ES / 16;         // 16-byte chunks per key row
   constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor, gfx9 family
   const int v_dg = tid & 15, v_kq = tid >> 4;
   const bool v_role = v_dg < D / 8;
+  const float v_inv = a.scales[3 * a.heads + h];    // bf16 values: 2^-e of the head
   // the descriptors are wavefront-uniform; say so, or every load gets a
   // readfirstlane loop around it
-  const int nrec = __builtin_amdgcn_readfirstlane(kend * D);
+  const int nrec = __builtin_amdgcn_readfirstlane(kend * D * ES);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kplane), 0, nrec, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -295,21 +365,27 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
 #pragma unroll
   for (int p = 0; p < KPASS; ++p) {
     const int c = tid + p * 256;
-    koff[p] = (c / (D / 16)) * D + 16 * (c % (D / 16));
+    koff[p] = (c / KCH) * D * ES + 16 * (c % KCH);
   }
-  const int voff = 4 * v_kq * D + 8 * v_dg;
+  const int voff = (4 * v_kq * D + 8 * v_dg) * ES;
   uint4 pk[KPASS];
   uint2 pv[4];
+  uint4 pvb[4];      // bf16 values: 8 dims of one key per load
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      auto w = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[p], kt * D, 0);
+      auto w = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[p], kt * D * ES, 0);
       pk[p] = uint4{w[0], w[1], w[2], w[3]};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      auto w = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff + j * D, kt * D, 0);
-      pv[j] = uint2{w[0], w[1]};
+      if constexpr (BF) {
+        auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + j * D * ES, kt * D * ES, 0);
+        pvb[j] = uint4{w[0], w[1], w[2], w[3]};
+      } else {
+        auto w = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff + j * D, kt * D, 0);
+        pv[j] = uint2{w[0], w[1]};
+      }
     }
   };
   // Staging of a loaded tile into LDS buffer buf, in parts so that the pieces
@@ -318,21 +394,36 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   auto store_k = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      const int c = tid + p * 256, key = c / (D / 16), col = c % (D / 16);
-      *reinterpret_cast<uint4 *>(sK[buf] + key * KSTRIDE + 16 * col) = pk[p];
+      const int c = tid + p * 256, key = c / KCH, col = c % KCH;
+      *reinterpret_cast<uint4 *>(sK[buf] + key * KROW + 16 * col) = pk[p];
     }
   };
   // row 4 v_kq + j has (row & 3) == j; the fp8 -> fp16 widening happens right
   // before the store, so only the loaded codes stay live between the phases
   auto store_v = [&](int buf, int j) __attribute__((always_inline)) {
     if (v_role) {
-      const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, false);
-      const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, true);
-      const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, false);
-      const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, true);
-      *reinterpret_cast<uint4 *>(sV[buf] + (4 * v_kq + j) * D + 8 * vchunk<D>(j, v_dg)) =
-          uint4{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
-                __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
+      uint4 w16;
+      if constexpr (BF) {
+        // bf16 -> fp32 (exact) -> times the head's power-of-two factor
+        // (exact) -> clamp to the fp16 range -> fp16
+        const uint32_t u[4] = {pvb[j].x, pvb[j].y, pvb[j].z, pvb[j].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float f0 = __builtin_amdgcn_fmed3f(__uint_as_float(u[k] << 16) * v_inv, -65504.0f, 65504.0f);
+          const float f1 = __builtin_amdgcn_fmed3f(__uint_as_float(u[k] & 0xffff0000u) * v_inv, -65504.0f, 65504.0f);
+          o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){f0, f1}, v2h));
+        }
+        w16 = uint4{o[0], o[1], o[2], o[3]};
+      } else {
+        const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, false);
+        const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].x), 1.0f, true);
+        const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, false);
+        const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(pv[j].y), 1.0f, true);
+        w16 = uint4{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                    __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
+      }
+      *reinterpret_cast<uint4 *>(sV[buf] + (4 * v_kq + j) * D + 8 * vchunk<D>(j, v_dg)) = w16;
     }
   };
 
@@ -366,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   // K fragments of block kb (32 keys) of buffer buf: the A operand of the score
   // MFMAs, one 32-byte fragment per 64-dim half.
   auto read_k = [&](int buf, int kb, v8i kf[DH]) {
-    const uint8_t *krow = sK[buf] + (32 * kb + r) * KSTRIDE;
+    const uint8_t *krow = sK[buf] + (32 * kb + r) * KROW;
 #pragma unroll
     for (int dh = 0; dh < DH; ++dh) {
       const uint4 lo = *reinterpret_cast<const uint4 *>(krow + 64 * dh + 16 * hh);
@@ -375,10 +466,22 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
                    static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
     }
   };
+  // bf16 key fragments of block kb: dims 16 ks + 8 hh .. + 7 of key 32 kb + r
+  // for every 16-dim step (the A operand of the bf16 MFMA 32x32x16).
+  auto read_kb = [&](int buf, int kb, v8bf kfb[D / 16]) {
+    const uint8_t *krow = sK[buf] + (32 * kb + r) * KROW;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      kfb[ks] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4 *>(krow + 32 * ks + 16 * hh));
+  };
   // Score MFMA i of a block (dim half i / 3, query term i % 3): S^T for the
   // block's 32 keys x this wave's 32 queries, in log2 units; register i of s
   // holds key 8(i/4) + 4hh + (i%4). Term t's B-side scale is byte t of
   // qscale[dh] (op_sel).
+  // bf16 score MFMA i: 16-dim step i / 2, query term i % 2.
+  auto qk_step_bf = [&](const v8bf kfb[D / 16], int i, v16f &s) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfb[i / 2], qb[i % 2][i / 2], i == 0 ? v16f{} : s, 0, 0, 0);
+  };
   auto qk_step = [&](const v8i kf[DH], int i, v16f &s) {
     const int dh = i / 3;
     switch (i % 3) {
@@ -451,12 +554,14 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
   // (j < 4), the same for A (V^T rows from LDS, one 16-byte read) and B (P^T
   // from the score registers); register 8(m%2)+j of the block is key 16m +
   // 8(j/4) + 4hh + (j%4).
-  constexpr int NQK = 3 * DH;           // score MFMAs per block
+  constexpr int NQK = BF ? D / 8 : 3 * DH;   // score MFMAs per block
   constexpr int NDB = D / 32;           // PV MFMAs per 16 keys
   auto region = [&](const v16f &s_cur, v16f &s_next, float &tmax_next, int qbuf, int qkb, int vbuf, int kb,
                     bool stage, int sbuf, bool load, int kt_load) {
     v8i kf[DH];
-    read_k(qbuf, qkb, kf);
+    v8bf kfb[BF ? D / 16 : 1];
+    if constexpr (BF) read_kb(qbuf, qkb, kfb);
+    else read_k(qbuf, qkb, kf);
     v8h va[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) va[db] = read_vt(vbuf, 32 * kb, db);
@@ -468,7 +573,8 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      qk_step(kf, i, s_next);
+      if constexpr (BF) qk_step_bf(kfb, i, s_next);
+      else qk_step(kf, i, s_next);
       if (load && i == 0) load_tile(kt_load);
       if (i < 4) exp4(s_cur, 4 * i, pw + 2 * i);
       if (i == NQK - 1) {
@@ -510,10 +616,17 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttendLaunch a) {
     v16f s0, s1;
     float t0, t1;
     {
-      v8i kf[DH];
-      read_k(0, 0, kf);
+      if constexpr (BF) {
+        v8bf kfb[D / 16];
+        read_kb(0, 0, kfb);
 #pragma unroll
-      for (int i = 0; i < NQK; ++i) qk_step(kf, i, s0);
+        for (int i = 0; i < NQK; ++i) qk_step_bf(kfb, i, s0);
+      } else {
+        v8i kf[DH];
+        read_k(0, 0, kf);
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) qk_step(kf, i, s0);
+      }
       t0 = block_max(s0);
     }
     // Tile t sits in buffer t % 3. Block 2t's region scores block 2t+1 and
@@ -672,13 +785,23 @@ hipError_t launch_attend(const AttendLaunch &a, hipStream_t st) {
   const unsigned prep_threads = static_cast<unsigned>(a.n_q) * a.heads * (a.head_dim / 8);
   const dim3 prep_grid((prep_threads + 255) / 256);
   const bool merge = a.split_lo > 1 || a.split_x > 0;
-  if (a.head_dim == 128) {
+  if (a.storage == kBF16) {
+    if (a.head_dim == 128) {
+      hipLaunchKernelGGL(query_prep_bf16_kernel<128>, prep_grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attend_kernel<128, kBF16>), grid, dim3(256), 0, st, a);
+      if (merge) launch_combine<128>(a, st);
+    } else {
+      hipLaunchKernelGGL(query_prep_bf16_kernel<64>, prep_grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attend_kernel<64, kBF16>), grid, dim3(256), 0, st, a);
+      if (merge) launch_combine<64>(a, st);
+    }
+  } else if (a.head_dim == 128) {
     hipLaunchKernelGGL(query_prep_kernel<128>, prep_grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_kernel<128, kE4M3>), grid, dim3(256), 0, st, a);
     if (merge) launch_combine<128>(a, st);
   } else {
     hipLaunchKernelGGL(query_prep_kernel<64>, prep_grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_kernel<64, kE4M3>), grid, dim3(256), 0, st, a);
     if (merge) launch_combine<64>(a, st);
   }
   return hipGetLastError();

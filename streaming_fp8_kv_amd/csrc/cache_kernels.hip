@@ -70,16 +70,25 @@ __device__ inline void decode4(uint32_t w, float *x) {
   x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as one word of bf16 (round to nearest, ties to even).
+__device__ inline uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 __device__ inline float scaled(float x, float inv) {
 #pragma clang fp contract(off)
   return x * inv;
 }
 
 // One thread = 16 consecutive dims of one (token, head): 32 B of bf16 K and of V
-// in, 16 B of K codes and 16 B of V codes out. Consecutive threads walk the
-// dims of a head, then the heads of a token, so the reads are fully coalesced
-// and each 128-byte row of a code plane is written by 8 adjacent lanes.
-template <int DT>   // input dtype, 0 bf16, 1 fp32: straight-line loads
+// in, 16 B of K codes and 16 B of V codes out (32 B each with bf16 storage).
+// Consecutive threads walk the dims of a head, then the heads of a token, so
+// the reads are fully coalesced and each row of a code plane is written by 8
+// adjacent lanes.
+template <int DT, int ST>   // input dtype (0 bf16, 1 fp32) and Storage: straight-line code
 __global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
   // 32-bit indexing: the host keeps every code plane below 2^31 bytes.
   const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 4;
@@ -114,6 +123,20 @@ __global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
   for (int j = 0; j < 4; ++j) {
     rotate_pair(x[4 * j], x[4 * j + 1], RopePair{cs[j].x, cs[j].y});
     rotate_pair(x[4 * j + 2], x[4 * j + 3], RopePair{cs[j].z, cs[j].w});
+  }
+  if constexpr (ST == kBF16) {
+    // bfloat16 storage: the rotated key and the value, each rounded once
+    uint4 k0, k1, v0, v1;
+    k0 = uint4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+    k1 = uint4{pack_bf16(x[8], x[9]), pack_bf16(x[10], x[11]), pack_bf16(x[12], x[13]), pack_bf16(x[14], x[15])};
+    v0 = uint4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+    v1 = uint4{pack_bf16(y[8], y[9]), pack_bf16(y[10], y[11]), pack_bf16(y[12], y[13]), pack_bf16(y[14], y[15])};
+    uint4 *kd = reinterpret_cast<uint4 *>(a.k8 + 2 * out_off);
+    uint4 *vd = reinterpret_cast<uint4 *>(a.v8 + 2 * out_off);
+    kd[0] = k0; kd[1] = k1;
+    vd[0] = v0; vd[1] = v1;
+    if (h == 0 && c == 0) a.pos[slot] = p;
+    return;
   }
   uint4 kw, vw;
   kw.x = encode4(scaled(x[0], inv_k), scaled(x[1], inv_k), scaled(x[2], inv_k), scaled(x[3], inv_k));
@@ -167,7 +190,16 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibrateLaunch a) {
     for (int w = 1; w < (blockDim.x >> 6); ++w) m = fmaxf(m, partial[w]);
     m = fmaxf(m, partial[0]);
     float scale = 1.0f, inv = 1.0f;
-    if (m > 0.0f) {
+    if (m > 0.0f && a.storage == kBF16) {
+      // power of two 2^e with m * 2^-e in [256, 512): moves bf16 values into
+      // fp16 range exactly when the attention stages them
+      int ex;
+      frexp(static_cast<double>(m), &ex);   // m = f * 2^ex, f in [0.5, 1)
+      int e = ex - 9;
+      e = e < -126 ? -126 : (e > 127 ? 127 : e);
+      scale = ldexpf(1.0f, e);
+      inv = ldexpf(1.0f, -e);
+    } else if (m > 0.0f) {
       scale = static_cast<float>(static_cast<double>(m) / 448.0);
       inv = static_cast<float>(448.0 / static_cast<double>(m));
     }
@@ -185,37 +217,50 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibrateLaunch a) {
 // contiguous kilobyte per wave. Each code pair is decoded exactly to fp32,
 // rotated by -delta, clamped and re-encoded in place; the per-head scale
 // cancels because the rotation is linear.
-template <int D>
+template <int D, int ST>
 __global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunch a) {
-  constexpr int CH = D / 16;            // 16-byte chunks per row
+  constexpr int ES = ST == kBF16 ? 2 : 1;       // bytes per element
+  constexpr int CH = D * ES / 16;       // 16-byte chunks per row
+  constexpr int PAIRS = 8 / ES;         // code pairs per 16-byte chunk
   constexpr int RSTEP = 64 / CH;        // rows one wave covers per step
   constexpr int J = 2;                  // steps per thread
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane % CH;
   const int slot0 = (blockIdx.x * 4 + wave) * (RSTEP * J) + lane / CH;
-  uint8_t *base = a.k8 + static_cast<size_t>(h) * a.capacity * D + c * 16;
-  const RopePair *cs = a.rope_row + c * 8;
-  RopePair t[8];
+  uint8_t *base = a.k8 + static_cast<size_t>(h) * a.capacity * D * ES + c * 16;
+  const RopePair *cs = a.rope_row + c * PAIRS;
+  RopePair t[PAIRS];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) t[k] = cs[k];
+  for (int k = 0; k < PAIRS; ++k) t[k] = cs[k];
   uint4 w[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int slot = slot0 + j * RSTEP;
-    if (slot < a.n_valid) w[j] = *reinterpret_cast<const uint4 *>(base + static_cast<size_t>(slot) * D);
+    if (slot < a.n_valid) w[j] = *reinterpret_cast<const uint4 *>(base + static_cast<size_t>(slot) * D * ES);
   }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int slot = slot0 + j * RSTEP;
-    if (slot < a.n_valid) {
+    if (slot < a.n_valid && ST == kBF16) {
+      const uint32_t u[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float x0 = __uint_as_float(u[k] << 16), x1 = __uint_as_float(u[k] & 0xffff0000u);   // exact
+        rotate_pair_back(x0, x1, t[k]);
+        o[k] = pack_bf16(x0, x1);
+      }
+      *reinterpret_cast<uint4 *>(base + static_cast<size_t>(slot) * D * ES) = uint4{o[0], o[1], o[2], o[3]};
+      if (h == 0 && c == 0) a.pos[slot] -= a.delta;
+    } else if (slot < a.n_valid) {
       float x[16];
       decode4(w[j].x, x);
       decode4(w[j].y, x + 4);
       decode4(w[j].z, x + 8);
       decode4(w[j].w, x + 12);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) rotate_pair_back(x[2 * k], x[2 * k + 1], t[k]);
+      for (int k = 0; k < PAIRS; ++k) rotate_pair_back(x[2 * k], x[2 * k + 1], t[k]);
       uint4 o;
       o.x = encode4(x[0], x[1], x[2], x[3]);
       o.y = encode4(x[4], x[5], x[6], x[7]);
@@ -251,8 +296,14 @@ inline unsigned blocks_for(size_t threads, unsigned per_block) {
 
 hipError_t launch_write(const WriteLaunch &a, hipStream_t s) {
   const size_t threads = static_cast<size_t>(a.n) * a.heads * (a.head_dim >> 4);
-  if (a.dtype == 0) hipLaunchKernelGGL(write_kernel<0>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(write_kernel<1>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, a);
+  const dim3 grid(blocks_for(threads, 256));
+  if (a.storage == kBF16) {
+    if (a.dtype == 0) hipLaunchKernelGGL((write_kernel<0, kBF16>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((write_kernel<1, kBF16>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.dtype == 0) hipLaunchKernelGGL((write_kernel<0, kE4M3>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((write_kernel<1, kE4M3>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -270,12 +321,18 @@ hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s) {
 
 hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s) {
   if (a.n_valid <= 0 || a.heads <= 0) return hipSuccess;
-  // rows per workgroup: 4 waves x (64 / (D/16)) rows x 2 steps
-  const int rows_per_block = 4 * (64 / (a.head_dim / 16)) * 2;
+  // rows per workgroup: 4 waves x (64 / (16-byte chunks per row)) rows x 2 steps
+  const int es = a.storage == kBF16 ? 2 : 1;
+  const int rows_per_block = 4 * (64 / (a.head_dim * es / 16)) * 2;
   const dim3 grid(static_cast<unsigned>((a.n_valid + rows_per_block - 1) / rows_per_block),
                   static_cast<unsigned>(a.heads));
-  if (a.head_dim == 128) hipLaunchKernelGGL(rebase_kernel<128>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(rebase_kernel<64>, grid, dim3(256), 0, s, a);
+  if (a.storage == kBF16) {
+    if (a.head_dim == 128) hipLaunchKernelGGL((rebase_kernel<128, kBF16>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rebase_kernel<64, kBF16>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.head_dim == 128) hipLaunchKernelGGL((rebase_kernel<128, kE4M3>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rebase_kernel<64, kE4M3>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -61,9 +61,13 @@ struct Layout {
   size_t k, v, pos, scale, total;
 };
 
+size_t elem_bytes(const sfkv_cache_cfg &c) { return c.storage == SFKV_STORE_BF16 ? 2 : 1; }
+
+int storage_of(const sfkv_cache_cfg &c) { return c.storage == SFKV_STORE_BF16 ? sfkv::kBF16 : sfkv::kE4M3; }
+
 Layout layout_of(const sfkv_cache_cfg &c) {
   Layout l;
-  const size_t plane = static_cast<size_t>(c.num_heads) * c.capacity * c.head_dim;
+  const size_t plane = static_cast<size_t>(c.num_heads) * c.capacity * c.head_dim * elem_bytes(c);
   l.k = 0;
   l.v = align_up(l.k + plane, 256);
   l.pos = align_up(l.v + plane, 256);
@@ -79,8 +83,10 @@ sfkv_status check_cfg(const sfkv_cache_cfg *c) {
   if (c->capacity < 1 || c->capacity > (1 << 24)) return fail(SFKV_EINVAL, "capacity must be in [1, 2^24]");
   if (c->max_new_tokens < 1 || c->max_new_tokens > c->capacity)
     return fail(SFKV_EINVAL, "max_new_tokens must be in [1, capacity]");
-  if (static_cast<size_t>(c->num_heads) * c->capacity * c->head_dim >= (size_t{1} << 31))
-    return fail(SFKV_EINVAL, "num_heads * capacity * head_dim must be below 2^31");
+  if (c->storage != SFKV_STORE_E4M3 && c->storage != SFKV_STORE_BF16)
+    return fail(SFKV_EINVAL, "storage must be SFKV_STORE_E4M3 or SFKV_STORE_BF16");
+  if (static_cast<size_t>(c->num_heads) * c->capacity * c->head_dim * elem_bytes(*c) >= (size_t{1} << 31))
+    return fail(SFKV_EINVAL, "one plane (num_heads * capacity * head_dim elements) must be below 2^31 bytes");
   return SFKV_OK;
 }
 
@@ -223,6 +229,7 @@ sfkv_status sfkv_calibrate_scales(sfkv_cache *c, const void *k, const void *v, s
   a.heads = c->cfg.num_heads;
   a.head_dim = c->cfg.head_dim;
   a.pos0 = static_cast<int>(c->next_pos);
+  a.storage = storage_of(c->cfg);
   a.rope = c->rope->table;
   a.scales = reinterpret_cast<float *>(c->base + c->scale_off);
   st = launched(sfkv::launch_calibrate(a, as_stream(stream)));
@@ -245,6 +252,7 @@ sfkv_status sfkv_cache_write(sfkv_cache *c, const void *k, const void *v, sfkv_d
   a.capacity = c->cfg.capacity;
   a.slot0 = static_cast<int>(c->tokens % c->cfg.capacity);
   a.pos0 = static_cast<int>(c->next_pos);
+  a.storage = storage_of(c->cfg);
   a.rope = c->rope->table;
   a.k8 = c->base + c->k_off;
   a.v8 = c->base + c->v_off;
@@ -266,7 +274,8 @@ static int n_valid_of(const sfkv_cache *c) {
 // Attend workspace, sized once per cache configuration for its largest write
 // and the device's CU count (a call with fewer queries or valid slots plans
 // fewer or equal workgroups, so one buffer serves every token count):
-//   query terms   [max_new][heads][3][head_dim] bytes
+//   query terms   [max_new][heads][3][head_dim] bytes (E4M3 storage) or
+//                 [max_new][heads][2][head_dim] bf16 (bf16 storage)
 //   query scales  [max_new][heads][head_dim/32] words
 //   split partials: O rows [workers][128][head_dim] fp32, then (max, sum)
 struct AttendWs {
@@ -279,7 +288,7 @@ static AttendWs attend_ws(const sfkv_cache_cfg &cfg, int cus) {
   w.slots = static_cast<size_t>(sfkv::attend_plan(cfg.max_new_tokens, cfg.num_heads, cfg.capacity, cus).workers);
   const size_t rows = w.slots * sfkv::kAttendQueriesPerBlock;
   w.qterm = 0;
-  w.qscale = align_up(qh * 3 * cfg.head_dim, 256);
+  w.qscale = align_up(qh * (cfg.storage == SFKV_STORE_BF16 ? 4 : 3) * cfg.head_dim, 256);
   w.part_o = align_up(w.qscale + qh * (cfg.head_dim / 32) * sizeof(uint32_t), 256);
   w.part_ml = align_up(w.part_o + rows * cfg.head_dim * sizeof(float), 256);
   w.total = align_up(w.part_ml + rows * 2 * sizeof(float), 256);
@@ -291,7 +300,7 @@ size_t sfkv_attend_workspace_bytes(const sfkv_cache *c) {
   return attend_ws(c->cfg, c->cus).total;
 }
 
-// One attend launch over FP8 planes laid out as layout_of(cfg) at `base`:
+// One attend launch over planes laid out as layout_of(cfg) at `base`:
 // n_valid slots, queries at positions qpos0 .. qpos0 + n_q - 1.
 static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_rope *rope, uint8_t *base,
                                  int nv, int64_t qpos0, const void *q, sfkv_dtype dtype, int32_t n_q,
@@ -309,6 +318,7 @@ static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_
   if (static_cast<size_t>(plan.workers) > ws.slots)
     return fail(SFKV_EINVAL, "attend plan exceeds the workspace (n_q or n_valid above the configured sizes)");
   sfkv::AttendLaunch a;
+  a.storage = storage_of(cfg);
   a.q = q;
   a.dtype = dtype;
   a.n_q = n_q;
@@ -349,6 +359,7 @@ sfkv_status sfkv_rebase_positions(sfkv_cache *c, int64_t delta, void *stream) {
     const int nv = n_valid_of(c);
     if (nv > 0) {
       sfkv::RebaseLaunch a;
+      a.storage = storage_of(c->cfg);
       a.k8 = c->base + c->k_off;
       a.pos = reinterpret_cast<int32_t *>(c->base + c->pos_off);
       a.heads = c->cfg.num_heads;
@@ -437,7 +448,7 @@ sfkv_status check_linear_frame(const sfkv_linear *c, const void *k, const void *
 }  // namespace
 
 size_t sfkv_linear_bytes(const sfkv_cache_cfg *cfg, sfkv_dtype dtype) {
-  if (check_cfg(cfg) != SFKV_OK) return 0;
+  if (check_cfg(cfg) != SFKV_OK || cfg->storage != SFKV_STORE_E4M3) return 0;
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return 0;
   return linear_layout_of(*cfg, dtype).total;
 }
@@ -448,6 +459,7 @@ sfkv_status sfkv_linear_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, s
   *out = nullptr;
   sfkv_status st = check_cfg(cfg);
   if (st != SFKV_OK) return st;
+  if (cfg->storage != SFKV_STORE_E4M3) return fail(SFKV_EINVAL, "the linear window keeps E4M3 storage only");
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
   if (!rope) return fail(SFKV_EINVAL, "rope is NULL");
   if (rope->head_dim != cfg->head_dim) return fail(SFKV_EINVAL, "rope head_dim differs from cfg head_dim");
@@ -493,6 +505,7 @@ sfkv_status sfkv_linear_calibrate_scales(sfkv_linear *c, const void *k, const vo
   a.heads = c->cfg.num_heads;
   a.head_dim = c->cfg.head_dim;
   a.pos0 = new_m - n;              // the window positions this frame would take
+  a.storage = sfkv::kE4M3;
   a.rope = c->rope->table;
   a.scales = reinterpret_cast<float *>(c->base + l.scale);
   st = launched(sfkv::launch_calibrate(a, as_stream(stream)));
@@ -533,6 +546,7 @@ sfkv_status sfkv_linear_write(sfkv_linear *c, const void *k, const void *v, int3
   a.capacity = c->cfg.capacity;
   a.slot0 = 0;
   a.pos0 = 0;
+  a.storage = sfkv::kE4M3;
   a.rope = c->rope->table;
   a.k8 = c->base + l.k;
   a.v8 = c->base + l.v;

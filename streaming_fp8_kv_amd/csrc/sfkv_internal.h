@@ -11,9 +11,14 @@ struct RopePair {
   float c, s;
 };
 
+// Storage of the cached keys and values: OCP E4M3 codes with per-head scales,
+// or bfloat16 (the non-FP8 variant).
+enum Storage { kE4M3 = 0, kBF16 = 1 };
+
 struct WriteLaunch {
   const void *k, *v;
   int dtype;        // 0 bf16, 1 fp32
+  int storage;      // Storage
   int n, heads, head_dim, capacity;
   int slot0;        // ring slot of token 0
   int pos0;         // position of token 0
@@ -26,11 +31,13 @@ struct WriteLaunch {
 struct CalibrateLaunch {
   const void *k, *v;
   int dtype, n, heads, head_dim, pos0;
+  int storage;      // kBF16: power-of-two factors instead of absmax / 448
   const RopePair *rope;
   float *scales;
 };
 
 struct RebaseLaunch {
+  int storage;
   uint8_t *k8;
   int32_t *pos;
   int heads, head_dim, capacity, n_valid;
@@ -39,6 +46,7 @@ struct RebaseLaunch {
 };
 
 struct AttendLaunch {
+  int storage;
   const void *q;
   int dtype, n_q, heads, head_dim, capacity, n_valid;
   int qpos0;                 // position of query row 0

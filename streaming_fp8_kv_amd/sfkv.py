@@ -47,9 +47,13 @@ SYMBOLS = (
 )
 
 
+STORE_E4M3, STORE_BF16 = 0, 1       # sfkv_storage
+
+
 class CacheConfig(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("capacity", ctypes.c_int32), ("max_new_tokens", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("max_new_tokens", ctypes.c_int32),
+                ("storage", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -245,9 +249,9 @@ class RingCache:
     """One ring cache: its device buffer, handle and views of its contents."""
 
     def __init__(self, rope: Rope, heads: int, capacity: int, max_new_tokens: Optional[int] = None,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, storage: int = STORE_E4M3):
         self.rope = rope
-        self.cfg = CacheConfig(heads, rope.head_dim, capacity, max_new_tokens or capacity)
+        self.cfg = CacheConfig(heads, rope.head_dim, capacity, max_new_tokens or capacity, storage)
         n = cache_bytes(self.cfg)
         if n == 0:
             raise ValueError("invalid cache configuration")
@@ -288,16 +292,22 @@ class RingCache:
     def state(self) -> dict:
         return cache_state(self.handle)
 
-    # views into the device buffer (no copies)
-    def k_codes(self) -> torch.Tensor:
+    # views into the device buffer (no copies); codes are uint8 E4M3 bytes or,
+    # with bf16 storage, int16 views of the bfloat16 bit patterns
+    def _plane(self, key: str) -> torch.Tensor:
         c = self.cfg
-        n = c.num_heads * c.capacity * c.head_dim
-        return self.buf[self.layout["k"]:self.layout["k"] + n].view(c.num_heads, c.capacity, c.head_dim)
+        es = 2 if c.storage == STORE_BF16 else 1
+        n = c.num_heads * c.capacity * c.head_dim * es
+        t = self.buf[self.layout[key]:self.layout[key] + n]
+        if es == 2:
+            t = t.view(torch.int16)
+        return t.view(c.num_heads, c.capacity, c.head_dim)
+
+    def k_codes(self) -> torch.Tensor:
+        return self._plane("k")
 
     def v_codes(self) -> torch.Tensor:
-        c = self.cfg
-        n = c.num_heads * c.capacity * c.head_dim
-        return self.buf[self.layout["v"]:self.layout["v"] + n].view(c.num_heads, c.capacity, c.head_dim)
+        return self._plane("v")
 
     def positions(self) -> torch.Tensor:
         c = self.cfg

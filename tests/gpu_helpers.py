@@ -2,10 +2,11 @@
 oracle twin, and the attention error metric.
 
 Parity bar (fixed here, used by every GPU test):
-  * FP8 code bytes, ring positions, scales and ring counters: bit-exact;
+  * stored code bytes (FP8, or bf16 in the non-FP8 storage), ring positions,
+    scales and ring counters: bit-exact;
   * attention, per call over the checked rows: max|o - r| / max|r| <= 2e-2 and
     mean|o - r| / mean|r| <= 1e-3, where r is the oracle's fp64 attention fed the
-    GPU's own FP8 cache and scales.
+    GPU's own cache (codes and scales).
 """
 from __future__ import annotations
 
@@ -14,7 +15,7 @@ import sys
 import numpy as np
 import torch
 
-from oracle import e4m3
+from oracle import bf16, e4m3
 from oracle.cache import RingCache as OracleCache, softmax_attention
 
 A_MAX = 2e-2
@@ -34,15 +35,26 @@ def attention_error(out: np.ndarray, ref: np.ndarray):
 class Mirror:
     """One GPU ring cache and an oracle cache over a subset of its heads."""
 
-    def __init__(self, sfkv, rope, spec, heads=None, max_new=None):
+    def __init__(self, sfkv, rope, spec, heads=None, max_new=None, storage="fp8"):
         s = spec.shape
         self.spec = spec
         self.H, self.d, self.C = s.heads, s.head_dim, s.capacity
         self.heads = list(range(s.heads)) if heads is None else list(heads)
+        self.bf16 = storage == "bf16"
         max_new = max_new or s.new_tokens
-        self.gpu = sfkv.RingCache(rope, s.heads, s.capacity, max_new)
+        self.gpu = sfkv.RingCache(rope, s.heads, s.capacity, max_new,
+                                  storage=sfkv.STORE_BF16 if self.bf16 else sfkv.STORE_E4M3)
         self.ora = OracleCache(len(self.heads), s.head_dim, s.capacity, max_new, s.rope_base,
-                               rope.max_position)
+                               rope.max_position, mode=storage)
+
+    def codes(self, which, nv=None):
+        """GPU codes of the checked heads as numpy (uint16 bf16 bit patterns or uint8)."""
+        hs = torch.tensor(self.heads)
+        t = (self.gpu.k_codes() if which == "k" else self.gpu.v_codes())[hs]
+        if nv is not None:
+            t = t[:, :nv]
+        a = t.cpu().numpy()
+        return a.view(np.uint16) if self.bf16 else a
 
     def _sub(self, t):
         return t[:, self.heads, :].float().numpy()
@@ -65,8 +77,8 @@ class Mirror:
         assert st == {"tokens": self.ora.tokens, "next_pos": self.ora.next_pos,
                       "write_slot": self.ora.write_slot, "n_valid": self.ora.n_valid}, tag
         hs = torch.tensor(self.heads)
-        k8 = self.gpu.k_codes()[hs].cpu().numpy()
-        v8 = self.gpu.v_codes()[hs].cpu().numpy()
+        k8 = self.codes("k")
+        v8 = self.codes("v")
         nv = self.ora.n_valid
         bad_k = np.count_nonzero(k8[:, :nv] != self.ora.k[:, :nv])
         bad_v = np.count_nonzero(v8[:, :nv] != self.ora.v[:, :nv])
@@ -80,11 +92,16 @@ class Mirror:
         """Oracle attention over the GPU's own codes and scales (checked heads)."""
         hs = torch.tensor(self.heads)
         nv = self.ora.n_valid
-        k8 = self.gpu.k_codes()[hs, :nv].cpu().numpy()
-        v8 = self.gpu.v_codes()[hs, :nv].cpu().numpy()
-        sc = self.gpu.scales()[:, hs].cpu().numpy().astype(np.float64)
-        kk = e4m3.decode(k8) * sc[0][:, None, None]
-        vv = e4m3.decode(v8) * sc[2][:, None, None]
+        k8 = self.codes("k", nv)
+        v8 = self.codes("v", nv)
+        if self.bf16:
+            # bf16 storage carries no quantisation scale
+            kk = bf16.decode(k8).astype(np.float64)
+            vv = bf16.decode(v8).astype(np.float64)
+        else:
+            sc = self.gpu.scales()[:, hs].cpu().numpy().astype(np.float64)
+            kk = e4m3.decode(k8) * sc[0][:, None, None]
+            vv = e4m3.decode(v8) * sc[2][:, None, None]
         qr = self.ora.rotated_queries(self._sub(q))[rows]
         return softmax_attention(qr, kk, vv)
 

@@ -50,6 +50,22 @@ def test_buffer_sizes(sfkv):
     assert sfkv.rope_bytes(64, 1024) == 1025 * 32 * 8
 
 
+def test_bf16_storage_sizes(sfkv):
+    # bf16 storage: two bytes per element in both planes, same positions and
+    # scale slots; the plane-size limit counts bytes, so it halves in tokens
+    cfg = sfkv.CacheConfig(24, 128, 5788, 757, sfkv.STORE_BF16)
+    plane = 2 * 24 * 5788 * 128
+    n = sfkv.cache_bytes(cfg)
+    assert n % 256 == 0
+    assert 2 * plane + 4 * 5788 + 16 * 24 <= n < 2 * plane + 4 * 5788 + 16 * 24 + 4 * 256
+    assert sfkv.cache_bytes(sfkv.CacheConfig(64, 128, 1 << 17, 16, sfkv.STORE_E4M3)) > 0   # 2^30 B
+    assert sfkv.cache_bytes(sfkv.CacheConfig(64, 128, 1 << 17, 16, sfkv.STORE_BF16)) == 0  # 2^31 B
+    for bad in (2, -1, 7):
+        assert sfkv.cache_bytes(sfkv.CacheConfig(24, 128, 5788, 757, bad)) == 0
+    # the plain linear window keeps E4M3 storage only
+    assert sfkv.linear_bytes(cfg, sfkv.BF16) == 0
+
+
 def test_linear_buffer_sizes(sfkv):
     cfg = sfkv.CacheConfig(24, 128, 5788, 757)
     planes = sfkv.cache_bytes(cfg)
