@@ -18,7 +18,9 @@ is up to three kernel launches (query prep, attention, split combine); the
 rocprofv3 summary lists each. cache_write alone, the same
 step captured once as a HIP graph and replayed, and the position reset (one
 delta rotation per cache) are timed in separate regions after the timed one and
-reported under ``extra``. So is the launch software's plain path on a sample of
+reported under ``extra``. So is the same sweep over rings that store bf16
+instead of E4M3 (``bf16_*``, the non-FP8 variant "Blackwell and Beyond Four
+GPUs" weighs), and the launch software's plain path on a sample of
 caches (``plain_*``): per call, the raw window is copy-shifted and every cached
 key re-rotated and re-quantised before the same attention, which is the upkeep
 the ring and write-time RoPE remove ("Where the Time Went"). ``cpu_baseline``
@@ -53,6 +55,8 @@ def parse():
     ap.add_argument("--calls", type=int, default=240, help="caches (calls) per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-calls", type=int, default=32)
+    ap.add_argument("--bf16-steps", type=int, default=5,
+                    help="timed steps of the same sweep over bf16 rings (0 skips)")
     ap.add_argument("--plain-calls", type=int, default=24,
                     help="caches for the plain-path (linear window) comparison; 0 skips it")
     return ap.parse_args()
@@ -131,6 +135,37 @@ def plain_path(sfkv, W, spec, n_caches: int, stream):
     attend = sum(b.elapsed_time(e) for _, b, e in ev) * 1e3 / len(ev)
     del caches
     return {"upkeep_us": upkeep, "attend_us": attend}
+
+
+def bf16_sweep(sfkv, W, spec, n_calls: int, steps: int, stream):
+    """The same 240-call step over caches that store bf16 instead of E4M3 (the
+    non-FP8 variant): two untimed steps, then `steps` timed ones, with events
+    around every attend call of the first timed step."""
+    import torch
+    from streaming_fp8_kv_amd.sweep import Sweep
+    E = torch.cuda.Event
+    sw = Sweep(sfkv, n_caches=n_calls, spec=spec, storage=sfkv.STORE_BF16)
+    sw.prefill()
+    for _ in range(2):
+        sw.step(stream)
+    torch.cuda.synchronize()
+    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
+    ev0, ev1 = E(enable_timing=True), E(enable_timing=True)
+    ev0.record(stream)
+    for step in range(steps):
+        for i, (c, (q, k, v), out) in enumerate(zip(sw.caches, sw.frames, sw.outs)):
+            sfkv.cache_write(c.handle, k, v, stream)
+            if step == 0:
+                att[i][0].record(stream)
+            sfkv.attend(c.handle, q, out, sw.workspace, stream)
+            if step == 0:
+                att[i][1].record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    attend_us = sum(a.elapsed_time(b) for a, b in att) * 1e3 / len(att)
+    del sw
+    return {"ms_per_step": ms, "attend_us": attend_us}
 
 
 def main():
@@ -226,6 +261,13 @@ def main():
     rebase_us = sum(a.elapsed_time(b) for a, b in rb) * 1e3 / len(rb)
 
     plain = plain_path(sfkv, W, spec, args.plain_calls, stream) if args.plain_calls > 0 else None
+    if args.bf16_steps > 0:
+        print("# bf16 rings", file=sys.stderr, flush=True)
+        del sw
+        torch.cuda.empty_cache()
+        bf = bf16_sweep(sfkv, W, spec, n_calls, args.bf16_steps, stream)
+    else:
+        bf = None
 
     n, H, d, C = s.new_tokens, s.heads, s.head_dim, s.capacity
     attend_flops = 4.0 * n * C * H * d
@@ -272,6 +314,13 @@ def main():
             "plain_attend_us": round(plain["attend_us"], 3),
             "plain_us_per_call": round(plain["upkeep_us"] + plain["attend_us"], 3),
             "plain_upkeep_ms_per_step": round(plain["upkeep_us"] * n_calls / 1e3, 4),
+        })
+    if bf is not None:
+        line["extra"].update({
+            "bf16_ms_per_step": round(bf["ms_per_step"], 4),
+            "bf16_us_per_call": round(bf["ms_per_step"] * 1e3 / n_calls, 3),
+            "bf16_attend_us": round(bf["attend_us"], 3),
+            "bf16_attend_tflops": round(attend_flops / (bf["attend_us"] * 1e-6) / 1e12, 2),
         })
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)

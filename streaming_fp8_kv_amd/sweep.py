@@ -8,7 +8,8 @@ after another because in the model each block depends on the previous one.
 
 Inputs are drawn on the device from per-cache seeded generators (seed
 ``spec.seed * 1000 + cache index``) with the production-call distribution.
-Every cache is calibrated on its first frame and prefilled with
+``storage`` picks the cache storage for every cache (E4M3 codes, the
+default, or bf16). Every cache is calibrated on its first frame and prefilled with
 ``spec.prefill_frames`` frames, so the ring has wrapped before the first timed
 step. A timed step writes each cache's step frame at the next positions and
 attends its queries over the whole ring.
@@ -24,13 +25,14 @@ from . import workloads as W
 
 class Sweep:
     def __init__(self, sfkv, n_caches: int = W.CALLS_PER_STEP, spec: W.WorkloadSpec = W.SWEEP,
-                 keep_frames_of: Iterable[int] = (), device: str = "cuda"):
+                 keep_frames_of: Iterable[int] = (), device: str = "cuda", storage: int = 0):
         s = spec.shape
         self.spec = spec
         self.sfkv = sfkv
         self.n = s.new_tokens
         self.rope = sfkv.Rope(s.head_dim, s.max_position, s.rope_base, device=device)
-        self.caches = [sfkv.RingCache(self.rope, s.heads, s.capacity, s.new_tokens, device=device)
+        self.caches = [sfkv.RingCache(self.rope, s.heads, s.capacity, s.new_tokens, device=device,
+                                      storage=storage)
                        for _ in range(n_caches)]
         need = self.caches[0].workspace_bytes()
         # one workspace serves every call: the calls are ordered on one stream
