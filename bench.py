@@ -42,9 +42,9 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 # rocprofv3 --pmc passes over this benchmark: FETCH_SIZE scaled by 2.0335 (a
 # plain copy kernel of 17.78 MB read reads 8,538.8 KiB of FETCH_SIZE) and
 # WRITE_SIZE as counted (the same copy's 17.78 MB write reads 17,363.3 KiB):
-# fetch 5.57 + 59.36 + 29.01 MB, write 7.27 + 28.58 + 9.30 MB. Set to None
+# fetch 5.57 + 61.69 + 37.92 MB, write 7.27 + 33.59 + 9.30 MB. Set to None
 # whenever the attend kernels change until the counters are taken again.
-ATTEND_TRAFFIC_BYTES = 139.09e6
+ATTEND_TRAFFIC_BYTES = 155.35e6
 
 
 def parse():
