@@ -668,24 +668,44 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
         *reinterpret_cast<float4 *>(o + 32 * db + 8 * j + 4 * hh) = v;
       }
   } else {
+    // The partial is stored normalised, O / l, in fp16: its entries are
+    // weighted means of fp16 values (at most 65504 in magnitude), and half the
+    // bytes of fp32 leave the L2 at the end of the launch and come back in the
+    // merge. An empty key range (l = 0) stores zeros.
+    const float f = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const size_t row = static_cast<size_t>(slot) * BQB + wave * 32 + r;
-    float *o = a.part_o + row * D;
+    uint16_t *o = a.part_o + row * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float4 v = {oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
-        *reinterpret_cast<float4 *>(o + 32 * db + 8 * j + 4 * hh) = v;
+        const v2h lo = __builtin_convertvector((float2_t){oacc[db][4 * j] * f, oacc[db][4 * j + 1] * f}, v2h);
+        const v2h hi = __builtin_convertvector((float2_t){oacc[db][4 * j + 2] * f, oacc[db][4 * j + 3] * f}, v2h);
+        *reinterpret_cast<uint2 *>(o + 32 * db + 8 * j + 4 * hh) =
+            uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       }
     if (hh == 0) *reinterpret_cast<float2 *>(a.part_ml + 2 * row) = float2{m_ref, l_tot};
   }
 }
 
 // Merge of the split partials: one thread per 8 output dims of one (query,
-// head) row; the row's pair has nsplit ranges in consecutive partial slots.
+// head) row; the row's pair has nsplit ranges in consecutive partial slots,
+// each holding (m, l) and the normalised O / l in fp16, so range s weighs
+// l_s 2^(m_s - max m).
 // NS > 0 bounds the split count at compile time so every load is issued at
 // once (slots past nsplit re-read slot 0 and get weight 0); pairs with a single
 // range were written directly.
+// acc[j] += w * (fp16 element j of the 8 in o)
+__device__ inline void add8(float acc[8], float w, uint4 o) {
+  const uint32_t u[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const v2h h = __builtin_bit_cast(v2h, u[k]);
+    acc[2 * k] += w * static_cast<float>(h[0]);
+    acc[2 * k + 1] += w * static_cast<float>(h[1]);
+  }
+}
+
 template <int D, int NS>
 __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
   constexpr int BQB = kAttendQueriesPerBlock;
@@ -706,14 +726,12 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
   if (NS > 0) {
     // every partial of the row is loaded before any arithmetic
     float2 ml[NS > 0 ? NS : 1];
-    float4 o0[NS > 0 ? NS : 1], o1[NS > 0 ? NS : 1];
+    uint4 ob[NS > 0 ? NS : 1];
 #pragma unroll
     for (int sp = 0; sp < NS; ++sp) {
       const size_t prow = base + static_cast<size_t>(sp < nsplit ? sp : 0) * BQB;
       ml[sp] = *reinterpret_cast<const float2 *>(a.part_ml + 2 * prow);
-      const float4 *o = reinterpret_cast<const float4 *>(a.part_o + prow * D + 8 * c8);
-      o0[sp] = o[0];
-      o1[sp] = o[1];
+      ob[sp] = *reinterpret_cast<const uint4 *>(a.part_o + prow * D + 8 * c8);
     }
     float mstar = kNegBig;
 #pragma unroll
@@ -721,10 +739,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
       if (sp < nsplit) mstar = fmaxf(mstar, ml[sp].x);
 #pragma unroll
     for (int sp = 0; sp < NS; ++sp) {
-      const float w = sp < nsplit ? __builtin_amdgcn_exp2f(ml[sp].x - mstar) : 0.0f;
-      L += w * ml[sp].y;
-      acc[0] += w * o0[sp].x; acc[1] += w * o0[sp].y; acc[2] += w * o0[sp].z; acc[3] += w * o0[sp].w;
-      acc[4] += w * o1[sp].x; acc[5] += w * o1[sp].y; acc[6] += w * o1[sp].z; acc[7] += w * o1[sp].w;
+      const float w = sp < nsplit ? __builtin_amdgcn_exp2f(ml[sp].x - mstar) * ml[sp].y : 0.0f;
+      L += w;
+      add8(acc, w, ob[sp]);
     }
   } else {
     float mstar = kNegBig;
@@ -733,12 +750,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
     for (int sp = 0; sp < nsplit; ++sp) {
       const size_t prow = base + static_cast<size_t>(sp) * BQB;
       const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * prow);
-      const float w = __builtin_amdgcn_exp2f(ml.x - mstar);
-      L += w * ml.y;
-      const float4 *o = reinterpret_cast<const float4 *>(a.part_o + prow * D + 8 * c8);
-      const float4 p0 = o[0], p1 = o[1];
-      acc[0] += w * p0.x; acc[1] += w * p0.y; acc[2] += w * p0.z; acc[3] += w * p0.w;
-      acc[4] += w * p1.x; acc[5] += w * p1.y; acc[6] += w * p1.z; acc[7] += w * p1.w;
+      const float w = __builtin_amdgcn_exp2f(ml.x - mstar) * ml.y;
+      L += w;
+      add8(acc, w, *reinterpret_cast<const uint4 *>(a.part_o + prow * D + 8 * c8));
     }
   }
   const float f = a.scales[2 * a.heads + h] / L;

@@ -277,7 +277,7 @@ static int n_valid_of(const sfkv_cache *c) {
 //   query terms   [max_new][heads][3][head_dim] bytes (E4M3 storage) or
 //                 [max_new][heads][2][head_dim] bf16 (bf16 storage)
 //   query scales  [max_new][heads][head_dim/32] words
-//   split partials: O rows [workers][128][head_dim] fp32, then (max, sum)
+//   split partials: O / l rows [workers][128][head_dim] fp16, then (max, sum)
 struct AttendWs {
   size_t qterm, qscale, part_o, part_ml, total, slots;
 };
@@ -290,7 +290,7 @@ static AttendWs attend_ws(const sfkv_cache_cfg &cfg, int cus) {
   w.qterm = 0;
   w.qscale = align_up(qh * (cfg.storage == SFKV_STORE_BF16 ? 4 : 3) * cfg.head_dim, 256);
   w.part_o = align_up(w.qscale + qh * (cfg.head_dim / 32) * sizeof(uint32_t), 256);
-  w.part_ml = align_up(w.part_o + rows * cfg.head_dim * sizeof(float), 256);
+  w.part_ml = align_up(w.part_o + rows * cfg.head_dim * sizeof(uint16_t), 256);
   w.total = align_up(w.part_ml + rows * 2 * sizeof(float), 256);
   return w;
 }
@@ -338,7 +338,7 @@ static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_
   uint8_t *wsb = static_cast<uint8_t *>(workspace);
   a.qterm = wsb + ws.qterm;
   a.qscale = reinterpret_cast<uint32_t *>(wsb + ws.qscale);
-  a.part_o = reinterpret_cast<float *>(wsb + ws.part_o);
+  a.part_o = reinterpret_cast<uint16_t *>(wsb + ws.part_o);
   a.part_ml = reinterpret_cast<float *>(wsb + ws.part_ml);
   return launched(sfkv::launch_attend(a, as_stream(stream)));
 }

@@ -56,7 +56,7 @@ struct AttendLaunch {
   float *out;
   int workers;               // attention workgroups (see AttendPlan)
   int split_lo, split_x;     // the plan's s_lo and x
-  float *part_o;             // [workers][128 rows][head_dim] split partials
+  uint16_t *part_o;          // [workers][128 rows][head_dim] fp16 split partials, O / l
   float *part_ml;            // [workers][128 rows][2] (max, sum)
   uint8_t *qterm;            // [n_q][heads][3][head_dim] E4M3 query terms
   uint32_t *qscale;          // [n_q][heads][head_dim/32] E8M0 scales, byte t = term t
