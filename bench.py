@@ -9,22 +9,24 @@ so the rings have wrapped. Inputs are synthetic, drawn on the device, and are
 resident before the timed region starts.
 
 Prints one JSON line. ``value`` is microseconds per cache_write + attend call
-(step time / 240). ``roofline`` is for attend, the dominant call: algorithmic
-FLOPs per call (4 * n * slots * heads * head_dim) over its average duration
-from HIP events recorded around every attend call of the first and the last
-timed step, on the stream the kernels run on, against the dense FP8 MFMA
-peak. One attend call
-is up to three kernel launches (query prep, attention, split combine); the
-rocprofv3 summary lists each. cache_write alone, the same
-step captured once as a HIP graph and replayed, and the position reset (one
-delta rotation per cache) are timed in separate regions after the timed one and
-reported under ``extra``. So is the same sweep over rings that store bf16
-instead of E4M3 (``bf16_*``, the non-FP8 variant "Blackwell and Beyond Four
-GPUs" weighs), and the launch software's plain path on a sample of
-caches (``plain_*``): per call, the raw window is copy-shifted and every cached
-key re-rotated and re-quantised before the same attention, which is the upkeep
-the ring and write-time RoPE remove ("Where the Time Went"). ``cpu_baseline``
-times the CPU oracle on a bounded sample.
+(step time / 240), each call made through the fused sfkv_write_attend entry
+point (the write's launch also prepares the frame's queries; same bits as the
+two separate calls). The same step as separate cache_write and attend calls is
+timed next (``unfused_*``). ``roofline`` is for attend, the dominant call:
+algorithmic FLOPs per call (4 * n * slots * heads * head_dim) over its average
+duration from HIP events recorded around each of one step's 240 separate
+attend calls, on the stream the kernels run on, against the dense FP8 MFMA
+peak. One separate attend call is three kernel launches (query prep,
+attention, split combine); the rocprofv3 summary lists each. cache_write
+alone, the fused step captured once as a HIP graph and replayed, and the
+position reset (one delta rotation per cache) are timed in separate regions
+after the timed one and reported under ``extra``. So is the same sweep over
+rings that store bf16 instead of E4M3 (``bf16_*``, the non-FP8 variant
+"Blackwell and Beyond Four GPUs" weighs), and the launch software's plain path
+on a sample of caches (``plain_*``): per call, the raw window is copy-shifted
+and every cached key re-rotated and re-quantised before the same attention,
+which is the upkeep the ring and write-time RoPE remove ("Where the Time
+Went"). ``cpu_baseline`` times the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -137,8 +139,8 @@ def plain_path(sfkv, W, spec, n_caches: int, stream):
 
 def bf16_sweep(sfkv, W, spec, n_calls: int, steps: int, stream):
     """The same 240-call step over caches that store bf16 instead of E4M3 (the
-    non-FP8 variant): two untimed steps, then `steps` timed ones, with events
-    around every attend call of the first timed step."""
+    non-FP8 variant): two untimed steps, `steps` timed fused steps, then one
+    step of separate calls with events around every attend call."""
     import torch
     from streaming_fp8_kv_amd.sweep import Sweep
     E = torch.cuda.Event
@@ -147,20 +149,20 @@ def bf16_sweep(sfkv, W, spec, n_calls: int, steps: int, stream):
     for _ in range(2):
         sw.step(stream)
     torch.cuda.synchronize()
-    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
     ev0, ev1 = E(enable_timing=True), E(enable_timing=True)
     ev0.record(stream)
-    for step in range(steps):
-        for i, (c, (q, k, v), out) in enumerate(zip(sw.caches, sw.frames, sw.outs)):
-            sfkv.cache_write(c.handle, k, v, stream)
-            if step == 0:
-                att[i][0].record(stream)
-            sfkv.attend(c.handle, q, out, sw.workspace, stream)
-            if step == 0:
-                att[i][1].record(stream)
+    for _ in range(steps):
+        sw.step(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
+    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
+    for (c, (q, k, v), out), (a0, a1) in zip(zip(sw.caches, sw.frames, sw.outs), att):
+        sfkv.cache_write(c.handle, k, v, stream)
+        a0.record(stream)
+        sfkv.attend(c.handle, q, out, sw.workspace, stream)
+        a1.record(stream)
+    torch.cuda.synchronize()
     attend_us = sum(a.elapsed_time(b) for a, b in att) * 1e3 / len(att)
     del sw
     return {"ms_per_step": ms, "attend_us": attend_us}
@@ -183,7 +185,7 @@ def main():
     sw = Sweep(sfkv, n_caches=n_calls, spec=spec)
     sw.prefill()
     torch.cuda.synchronize()
-    if sw.positions_left() < args.warmup + args.steps + 3:
+    if sw.positions_left() < args.warmup + args.steps + 5:
         raise SystemExit("too many steps for the position range; lower --steps/--warmup")
 
     stream = torch.cuda.current_stream()
@@ -191,30 +193,37 @@ def main():
         sw.step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps; events around every attend call of the first
-    # and the last step (each event pair costs a few microseconds of stream
-    # time, so recording them on every step would inflate the step time) ----
+    # ---- timed region: K steps of the fused write + attend call, no events
+    # inside (each event pair costs a few microseconds of stream time) ----
     E = torch.cuda.Event
     ev_start, ev_end = E(enable_timing=True), E(enable_timing=True)
-    sampled = sorted({0, args.steps - 1})
-    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(len(sampled) * n_calls)]
     torch.cuda.synchronize()
     ev_start.record(stream)
-    j = 0
-    for step in range(args.steps):
-        timed = step in sampled
+    for _ in range(args.steps):
         for c, (q, k, v), out in zip(sw.caches, sw.frames, sw.outs):
-            sfkv.cache_write(c.handle, k, v, stream)
-            if timed:
-                att[j][0].record(stream)
-            sfkv.attend(c.handle, q, out, sw.workspace, stream)
-            if timed:
-                att[j][1].record(stream)
-                j += 1
+            sfkv.write_attend(c.handle, k, v, q, out, sw.workspace, stream)
     ev_end.record(stream)
     torch.cuda.synchronize()
     total_ms = ev_start.elapsed_time(ev_end)
     ms_per_step = total_ms / args.steps
+
+    # ---- the same step as separate cache_write and attend calls: one step
+    # without events, then one with events around every attend call (the
+    # attend call's duration for the roofline) ----
+    u0, u1 = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    u0.record(stream)
+    sw.step(stream, fused=False)
+    u1.record(stream)
+    torch.cuda.synchronize()
+    unfused_ms = u0.elapsed_time(u1)
+    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
+    for (c, (q, k, v), out), (a0, a1) in zip(zip(sw.caches, sw.frames, sw.outs), att):
+        sfkv.cache_write(c.handle, k, v, stream)
+        a0.record(stream)
+        sfkv.attend(c.handle, q, out, sw.workspace, stream)
+        a1.record(stream)
+    torch.cuda.synchronize()
     attend_us = sum(a.elapsed_time(b) for a, b in att) * 1e3 / len(att)
 
     # ---- cache_write alone, one step's worth, events around every launch ----
@@ -300,6 +309,8 @@ def main():
             "rebase_us_per_cache": round(rebase_us, 3),
             "rebase_hbm_frac": round(rebase_bytes / (rebase_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "reset_step_extra_ms": round(rebase_us * n_calls / 1e3, 4),
+            "unfused_ms_per_step": round(unfused_ms, 4),
+            "unfused_us_per_call": round(unfused_ms * 1e3 / n_calls, 3),
             "graph_ms_per_step": round(graph_ms, 4),
             "graph_us_per_call": round(graph_ms * 1e3 / n_calls, 3),
             "ring_upkeep_ms_per_step": round(write_us * n_calls / 1e3, 4),

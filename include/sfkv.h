@@ -158,6 +158,21 @@ size_t sfkv_attend_workspace_bytes(const sfkv_cache *cache);
 sfkv_status sfkv_attend(sfkv_cache *cache, const void *q, sfkv_dtype dtype, int32_t n_q,
                         float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* sfkv_write_attend: one attention call's cache traffic as a single call:
+ * sfkv_cache_write(k, v, n) followed by sfkv_attend(q, n) on the frame just
+ * written, with the same result bit for bit. The write's launch also prepares
+ * the frame's queries, which saves one launch per call. k, v, q are
+ * [n][H][d] in `dtype`; `out` and `workspace` as for sfkv_attend.
+ * Errors: those of sfkv_cache_write and of sfkv_attend; on any of them nothing
+ * is enqueued and the state is unchanged. EHIP from the attention's launch
+ * leaves the write done (the state advanced).
+ * Source: "Where the Time Went" (each of the 240 calls per step writes its
+ * cache and attends over it); "Do It Once, at Write Time" (the frame is
+ * rotated once, as it enters the cache). */
+sfkv_status sfkv_write_attend(sfkv_cache *cache, const void *k, const void *v, const void *q,
+                              sfkv_dtype dtype, int32_t n, float *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* sfkv_rebase_positions: subtract delta from every position with one delta
  * rotation of the cached keys: each valid key's FP8 codes are rotated by
  * -delta*theta in the code domain (the per-head scale cancels), clamped and

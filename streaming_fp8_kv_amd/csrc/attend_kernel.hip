@@ -31,6 +31,7 @@
 //
 // Long key ranges are split across workgroups (split-KV) to fill the 256 CUs; a
 // second kernel merges the partial (max, sum, O) triples.
+#include "query_prep.h"
 #include "sfkv_internal.h"
 
 #include <cstdlib>
@@ -48,7 +49,6 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int BK = kAttendKeysPerTile;      // 64 keys per LDS tile
 constexpr int KSTRIDE = 144;                // bytes per key row in LDS (128 + 16 pad)
@@ -58,108 +58,18 @@ constexpr int KSTRIDE = 144;                // bytes per key row in LDS (128 + 1
 // row stores (16 lanes per row) are both free of bank conflicts at D = 128.
 template <int D>
 __device__ __forceinline__ int vchunk(int row, int c) { return c ^ ((4 * (row & 3)) & (D / 8 - 1)); }
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Smallest e with m * 2^-e <= 448, from the exact binary exponent of m
-// (448 = 0.875 * 2^9); clamped to the E8M0 range.
-__device__ inline int block_exponent(float m) {
-  if (!(m > 0.0f)) return 0;
-  int E;
-  float f = frexpf(m, &E);   // m = f * 2^E, f in [0.5, 1)
-  int e = (f <= 0.875f) ? E - 9 : E - 8;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// 8 consecutive query elements as fp32.
-__device__ inline void load8(const void *q, size_t elem, int dtype, float *x) {
-  if (dtype == 0) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + elem);
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { x[2 * j] = bf16_lo(u[j]); x[2 * j + 1] = bf16_hi(u[j]); }
-  } else {
-    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + elem);
-    const float4 v0 = p[0], v1 = p[1];
-    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-  }
-}
-
-// Max over the four lanes of an aligned lane quad (DPP quad permutations).
-__device__ inline float quad_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));  // [1,0,3,2]
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));  // [2,3,0,1]
-  return v;
-}
-
-// Query preparation, once per call: RoPE at the query's position, the factor
-// scale_k * log2(e) / sqrt(d) folded in, then three E4M3 terms, each the
-// rounding of what the earlier terms left over, each with one power-of-two
-// (E8M0) scale per 32-dim block (exactly one scale block of the 32x32x64
-// block-scaled MFMA). A three-term query carries about 12 significant bits.
-// One thread per 8 dims; the four threads of a block sit in one lane quad and
-// share the block maximum through DPP. Codes are stored in natural dim order,
-// [query][head][term][dim]; the scale bytes of terms 0..2 are packed into one
-// word per block.
+// Query preparation, once per call, as its own small kernel (the fused write +
+// attend call runs the same function inside the write's launch).
 template <int D>
 __global__ __launch_bounds__(256) void query_prep_kernel(AttendLaunch a) {
-  constexpr int NB = D / 32;
-  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
-  // the element count is a multiple of 4, so a lane quad is all in or all out
-  if (idx >= static_cast<unsigned>(a.n_q) * a.heads * (D / 8)) return;
-  const int g = idx & 3;                        // 8-dim group inside the block
-  const unsigned blk = idx >> 2;
-  const int b = blk % NB;
-  const unsigned qh = blk / NB;                 // qi * heads + h
-  const int h = qh % a.heads;
-  const int qi = qh / a.heads;
-  float x[8];
-  load8(a.q, static_cast<size_t>(qh) * D + 32 * b + 8 * g, a.dtype, x);
-  // A rebase can leave the last write's queries at negative positions;
-  // cos(-x) = cos(x) and sin(-x) = -sin(x) reuse the row of |p|.
-  const int qp = a.qpos0 + qi;
-  const float sgn = qp < 0 ? -1.0f : 1.0f;
-  const RopePair *row = a.rope + static_cast<size_t>(qp < 0 ? -qp : qp) * (D / 2) + 16 * b + 4 * g;
-  const float qs = a.scales[h] * kLog2e * (1.0f / sqrtf(static_cast<float>(D)));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    RopePair cs = row[j];
-    cs.s *= sgn;
-    const float u = x[2 * j], v = x[2 * j + 1];
-    x[2 * j] = (u * cs.c - v * cs.s) * qs;
-    x[2 * j + 1] = (u * cs.s + v * cs.c) * qs;
-  }
-  uint32_t packed = 0;
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
-    const int e = block_exponent(quad_max(m));
-    int w[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j], -e), ldexpf(x[4 * j + 1], -e), 0, false);
-      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j + 2], -e), ldexpf(x[4 * j + 3], -e), lo, true);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);
-      x[4 * j] -= ldexpf(lo[0], e);
-      x[4 * j + 1] -= ldexpf(lo[1], e);
-      x[4 * j + 2] -= ldexpf(hi[0], e);
-      x[4 * j + 3] -= ldexpf(hi[1], e);
-    }
-    *reinterpret_cast<uint2 *>(a.qterm + (static_cast<size_t>(qh) * 3 + t) * D + 32 * b + 8 * g) =
-        uint2{static_cast<uint32_t>(w[0]), static_cast<uint32_t>(w[1])};
-    packed |= static_cast<uint32_t>(127 + e) << (8 * t);
-  }
-  if (g == 0) a.qscale[static_cast<size_t>(qh) * NB + b] = packed;
+  qprep::prep_e4m3<D>(a, blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void query_prep_bf16_kernel(AttendLaunch a) {
+  qprep::prep_bf16<D>(a, blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // Q terms of one lane of a 32-query block (column r = lane & 31, half
@@ -190,41 +100,6 @@ __device__ inline void load_query_terms(const AttendLaunch &a, int h, int qi, in
                       static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
     }
   }
-}
-
-// Query preparation for a bfloat16 cache, once per call: RoPE at the query's
-// position, times log2(e) / sqrt(d) (the keys are used as stored, unscaled),
-// then two bf16 terms q = hi + lo with lo the rounding of what hi left over,
-// about 16 significant bits. Stored [query][head][term][dim] as bf16; one
-// thread per 8 dims.
-template <int D>
-__global__ __launch_bounds__(256) void query_prep_bf16_kernel(AttendLaunch a) {
-  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<unsigned>(a.n_q) * a.heads * (D / 8)) return;
-  const int g8 = idx % (D / 8);
-  const unsigned qh = idx / (D / 8);
-  const int qi = qh / a.heads;
-  float x[8];
-  load8(a.q, static_cast<size_t>(qh) * D + 8 * g8, a.dtype, x);
-  const int qp = a.qpos0 + qi;
-  const float sgn = qp < 0 ? -1.0f : 1.0f;
-  const RopePair *row = a.rope + static_cast<size_t>(qp < 0 ? -qp : qp) * (D / 2) + 4 * g8;
-  const float qs = kLog2e * (1.0f / sqrtf(static_cast<float>(D)));
-  uint32_t hi[4], lo[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    RopePair cs = row[j];
-    cs.s *= sgn;
-    const float u = x[2 * j], v = x[2 * j + 1];
-    const float a0 = (u * cs.c - v * cs.s) * qs, a1 = (u * cs.s + v * cs.c) * qs;
-    const v2bf h = __builtin_convertvector((float2_t){a0, a1}, v2bf);
-    const float r0 = a0 - static_cast<float>(h[0]), r1 = a1 - static_cast<float>(h[1]);
-    hi[j] = __builtin_bit_cast(uint32_t, h);
-    lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){r0, r1}, v2bf));
-  }
-  uint4 *dst = reinterpret_cast<uint4 *>(a.qterm + (static_cast<size_t>(qh) * 2 * D + 8 * g8) * 2);
-  dst[0] = uint4{hi[0], hi[1], hi[2], hi[3]};
-  dst[D / 8] = uint4{lo[0], lo[1], lo[2], lo[3]};
 }
 
 // bf16 query terms of one lane for every 16-dim step ks: dims 16 ks + 8 hh ..
@@ -799,22 +674,23 @@ hipError_t launch_attend(const AttendLaunch &a, hipStream_t st) {
   const unsigned prep_threads = static_cast<unsigned>(a.n_q) * a.heads * (a.head_dim / 8);
   const dim3 prep_grid((prep_threads + 255) / 256);
   const bool merge = a.split_lo > 1 || a.split_x > 0;
+  const bool prep = !a.queries_ready;
   if (a.storage == kBF16) {
     if (a.head_dim == 128) {
-      hipLaunchKernelGGL(query_prep_bf16_kernel<128>, prep_grid, dim3(256), 0, st, a);
+      if (prep) hipLaunchKernelGGL(query_prep_bf16_kernel<128>, prep_grid, dim3(256), 0, st, a);
       hipLaunchKernelGGL((attend_kernel<128, kBF16>), grid, dim3(256), 0, st, a);
       if (merge) launch_combine<128>(a, st);
     } else {
-      hipLaunchKernelGGL(query_prep_bf16_kernel<64>, prep_grid, dim3(256), 0, st, a);
+      if (prep) hipLaunchKernelGGL(query_prep_bf16_kernel<64>, prep_grid, dim3(256), 0, st, a);
       hipLaunchKernelGGL((attend_kernel<64, kBF16>), grid, dim3(256), 0, st, a);
       if (merge) launch_combine<64>(a, st);
     }
   } else if (a.head_dim == 128) {
-    hipLaunchKernelGGL(query_prep_kernel<128>, prep_grid, dim3(256), 0, st, a);
+    if (prep) hipLaunchKernelGGL(query_prep_kernel<128>, prep_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((attend_kernel<128, kE4M3>), grid, dim3(256), 0, st, a);
     if (merge) launch_combine<128>(a, st);
   } else {
-    hipLaunchKernelGGL(query_prep_kernel<64>, prep_grid, dim3(256), 0, st, a);
+    if (prep) hipLaunchKernelGGL(query_prep_kernel<64>, prep_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((attend_kernel<64, kE4M3>), grid, dim3(256), 0, st, a);
     if (merge) launch_combine<64>(a, st);
   }

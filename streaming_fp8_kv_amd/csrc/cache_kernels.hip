@@ -11,6 +11,7 @@
 // in a fixed order with no fused multiply-add (this file is compiled with
 // -ffp-contract=off and the rotations also carry the pragma), so the bytes are
 // reproducible by any other IEEE implementation of the same formulas.
+#include "query_prep.h"
 #include "sfkv_internal.h"
 
 namespace sfkv {
@@ -89,10 +90,9 @@ __device__ inline float scaled(float x, float inv) {
 // the reads are fully coalesced and each row of a code plane is written by 8
 // adjacent lanes.
 template <int DT, int ST>   // input dtype (0 bf16, 1 fp32) and Storage: straight-line code
-__global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
+__device__ inline void write_body(const WriteLaunch &a, unsigned idx) {
   // 32-bit indexing: the host keeps every code plane below 2^31 bytes.
   const unsigned chunks = static_cast<unsigned>(a.head_dim) >> 4;
-  const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
   const unsigned total = static_cast<unsigned>(a.n) * a.heads * chunks;
   if (idx >= total) return;
   const int c = static_cast<int>(idx % chunks);
@@ -151,6 +151,26 @@ __global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
   *reinterpret_cast<uint4 *>(a.v8 + out_off) = vw;
 
   if (h == 0 && c == 0) a.pos[slot] = p;
+}
+
+template <int DT, int ST>
+__global__ __launch_bounds__(256) void write_kernel(WriteLaunch a) {
+  write_body<DT, ST>(a, blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// The write of a frame and the preparation of the same frame's queries in one
+// launch (the fused write + attend call): workgroups [0, wblocks) write, the
+// rest prepare queries. The two parts touch disjoint memory; the query part
+// reads only the scales, which calibration wrote before.
+template <int DT, int ST, int D>
+__global__ __launch_bounds__(256) void write_prep_kernel(WriteLaunch w, AttendLaunch q, unsigned wblocks) {
+  if (blockIdx.x < wblocks) {
+    write_body<DT, ST>(w, blockIdx.x * blockDim.x + threadIdx.x);
+  } else {
+    const unsigned idx = (blockIdx.x - wblocks) * blockDim.x + threadIdx.x;
+    if constexpr (ST == kBF16) qprep::prep_bf16<D>(q, idx);
+    else qprep::prep_e4m3<D>(q, idx);
+  }
 }
 
 __device__ inline float wave_max(float m) {
@@ -303,6 +323,26 @@ hipError_t launch_write(const WriteLaunch &a, hipStream_t s) {
   } else {
     if (a.dtype == 0) hipLaunchKernelGGL((write_kernel<0, kE4M3>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((write_kernel<1, kE4M3>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int ST>
+void launch_write_prep_d(const WriteLaunch &w, const AttendLaunch &q, dim3 grid, unsigned wblocks, hipStream_t s) {
+  if (w.head_dim == 128) hipLaunchKernelGGL((write_prep_kernel<DT, ST, 128>), grid, dim3(256), 0, s, w, q, wblocks);
+  else hipLaunchKernelGGL((write_prep_kernel<DT, ST, 64>), grid, dim3(256), 0, s, w, q, wblocks);
+}
+
+hipError_t launch_write_prep(const WriteLaunch &w, const AttendLaunch &q, hipStream_t s) {
+  const unsigned wblocks = blocks_for(static_cast<size_t>(w.n) * w.heads * (w.head_dim >> 4), 256);
+  const unsigned qblocks = blocks_for(static_cast<size_t>(q.n_q) * q.heads * (q.head_dim / 8), 256);
+  const dim3 grid(wblocks + qblocks);
+  if (w.storage == kBF16) {
+    if (w.dtype == 0) launch_write_prep_d<0, kBF16>(w, q, grid, wblocks, s);
+    else launch_write_prep_d<1, kBF16>(w, q, grid, wblocks, s);
+  } else {
+    if (w.dtype == 0) launch_write_prep_d<0, kE4M3>(w, q, grid, wblocks, s);
+    else launch_write_prep_d<1, kE4M3>(w, q, grid, wblocks, s);
   }
   return hipGetLastError();
 }

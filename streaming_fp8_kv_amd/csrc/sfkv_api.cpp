@@ -237,11 +237,8 @@ sfkv_status sfkv_calibrate_scales(sfkv_cache *c, const void *k, const void *v, s
   return st;
 }
 
-sfkv_status sfkv_cache_write(sfkv_cache *c, const void *k, const void *v, sfkv_dtype dtype,
-                             int32_t n, void *stream) {
-  sfkv_status st = check_frame(c, k, v, dtype, n);
-  if (st != SFKV_OK) return st;
-  if (!c->calibrated) return fail(SFKV_ESTATE, "cache_write before calibrate_scales");
+static sfkv::WriteLaunch write_launch(const sfkv_cache *c, const void *k, const void *v, sfkv_dtype dtype,
+                                     int32_t n) {
   sfkv::WriteLaunch a;
   a.k = k;
   a.v = v;
@@ -258,12 +255,24 @@ sfkv_status sfkv_cache_write(sfkv_cache *c, const void *k, const void *v, sfkv_d
   a.v8 = c->base + c->v_off;
   a.pos = reinterpret_cast<int32_t *>(c->base + c->pos_off);
   a.scales = reinterpret_cast<const float *>(c->base + c->scale_off);
-  st = launched(sfkv::launch_write(a, as_stream(stream)));
-  if (st != SFKV_OK) return st;
+  return a;
+}
+
+static void advance(sfkv_cache *c, int32_t n) {
   c->last_pos0 = c->next_pos;
   c->last_n = n;
   c->tokens += n;
   c->next_pos += n;
+}
+
+sfkv_status sfkv_cache_write(sfkv_cache *c, const void *k, const void *v, sfkv_dtype dtype,
+                             int32_t n, void *stream) {
+  sfkv_status st = check_frame(c, k, v, dtype, n);
+  if (st != SFKV_OK) return st;
+  if (!c->calibrated) return fail(SFKV_ESTATE, "cache_write before calibrate_scales");
+  st = launched(sfkv::launch_write(write_launch(c, k, v, dtype, n), as_stream(stream)));
+  if (st != SFKV_OK) return st;
+  advance(c, n);
   return SFKV_OK;
 }
 
@@ -300,11 +309,12 @@ size_t sfkv_attend_workspace_bytes(const sfkv_cache *c) {
   return attend_ws(c->cfg, c->cus).total;
 }
 
-// One attend launch over planes laid out as layout_of(cfg) at `base`:
-// n_valid slots, queries at positions qpos0 .. qpos0 + n_q - 1.
-static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_rope *rope, uint8_t *base,
-                                 int nv, int64_t qpos0, const void *q, sfkv_dtype dtype, int32_t n_q,
-                                 float *out, void *workspace, size_t workspace_bytes, void *stream) {
+// Arguments of one attend launch over planes laid out as layout_of(cfg) at
+// `base`: n_valid slots, queries at positions qpos0 .. qpos0 + n_q - 1.
+// Validates and fills `a`; enqueues nothing.
+static sfkv_status attend_setup(const sfkv_cache_cfg &cfg, int cus, const sfkv_rope *rope, uint8_t *base,
+                                int nv, int64_t qpos0, const void *q, sfkv_dtype dtype, int32_t n_q,
+                                float *out, void *workspace, size_t workspace_bytes, sfkv::AttendLaunch &a) {
   if (!q || !out) return fail(SFKV_EINVAL, "q and out must be device pointers");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(SFKV_EINVAL, "q and out must be 16-byte aligned");
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
@@ -317,8 +327,8 @@ static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_
   const sfkv::AttendPlan plan = sfkv::attend_plan(n_q, cfg.num_heads, nv, cus);
   if (static_cast<size_t>(plan.workers) > ws.slots)
     return fail(SFKV_EINVAL, "attend plan exceeds the workspace (n_q or n_valid above the configured sizes)");
-  sfkv::AttendLaunch a;
   a.storage = storage_of(cfg);
+  a.queries_ready = 0;
   a.q = q;
   a.dtype = dtype;
   a.n_q = n_q;
@@ -340,6 +350,16 @@ static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_
   a.qscale = reinterpret_cast<uint32_t *>(wsb + ws.qscale);
   a.part_o = reinterpret_cast<uint16_t *>(wsb + ws.part_o);
   a.part_ml = reinterpret_cast<float *>(wsb + ws.part_ml);
+  return SFKV_OK;
+}
+
+static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_rope *rope, uint8_t *base,
+                                 int nv, int64_t qpos0, const void *q, sfkv_dtype dtype, int32_t n_q,
+                                 float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  sfkv::AttendLaunch a;
+  const sfkv_status st = attend_setup(cfg, cus, rope, base, nv, qpos0, q, dtype, n_q, out, workspace,
+                                      workspace_bytes, a);
+  if (st != SFKV_OK) return st;
   return launched(sfkv::launch_attend(a, as_stream(stream)));
 }
 
@@ -350,6 +370,25 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
   return attend_planes(c->cfg, c->cus, c->rope, c->base, n_valid_of(c), c->last_pos0, q, dtype, n_q, out,
                        workspace, workspace_bytes, stream);
+}
+
+sfkv_status sfkv_write_attend(sfkv_cache *c, const void *k, const void *v, const void *q, sfkv_dtype dtype,
+                              int32_t n, float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  sfkv_status st = check_frame(c, k, v, dtype, n);
+  if (st != SFKV_OK) return st;
+  if (!c->calibrated) return fail(SFKV_ESTATE, "write_attend before calibrate_scales");
+  // the attention sees the ring as this write leaves it
+  const int64_t after = c->tokens + n;
+  const int nv = static_cast<int>(after < c->cfg.capacity ? after : c->cfg.capacity);
+  sfkv::AttendLaunch a;
+  st = attend_setup(c->cfg, c->cus, c->rope, c->base, nv, c->next_pos, q, dtype, n, out, workspace,
+                    workspace_bytes, a);
+  if (st != SFKV_OK) return st;
+  st = launched(sfkv::launch_write_prep(write_launch(c, k, v, dtype, n), a, as_stream(stream)));
+  if (st != SFKV_OK) return st;
+  advance(c, n);
+  a.queries_ready = 1;
+  return launched(sfkv::launch_attend(a, as_stream(stream)));
 }
 
 sfkv_status sfkv_rebase_positions(sfkv_cache *c, int64_t delta, void *stream) {

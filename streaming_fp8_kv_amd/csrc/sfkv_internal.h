@@ -47,6 +47,7 @@ struct RebaseLaunch {
 
 struct AttendLaunch {
   int storage;
+  int queries_ready;         // nonzero: qterm / qscale already hold this call's query terms
   const void *q;
   int dtype, n_q, heads, head_dim, capacity, n_valid;
   int qpos0;                 // position of query row 0
@@ -78,6 +79,9 @@ hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s);
 hipError_t launch_write(const WriteLaunch &a, hipStream_t s);
 hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s);
 hipError_t launch_attend(const AttendLaunch &a, hipStream_t s);
+// One launch: the write `w` and the query preparation of `q` (the same frame's
+// queries), with q.queries_ready ignored.
+hipError_t launch_write_prep(const WriteLaunch &w, const AttendLaunch &q, hipStream_t s);
 
 // Attention tiling shared by the launcher and the workspace sizing.
 constexpr int kAttendQueriesPerBlock = 128;  // 4 waves x 32 queries

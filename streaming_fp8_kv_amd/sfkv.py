@@ -38,7 +38,7 @@ SYMBOLS = (
     "sfkv_rope_bytes", "sfkv_rope_init", "sfkv_rope_destroy",
     "sfkv_cache_bytes", "sfkv_cache_init", "sfkv_cache_destroy",
     "sfkv_calibrate_scales", "sfkv_cache_write",
-    "sfkv_attend_workspace_bytes", "sfkv_attend", "sfkv_rebase_positions",
+    "sfkv_attend_workspace_bytes", "sfkv_attend", "sfkv_write_attend", "sfkv_rebase_positions",
     "sfkv_cache_state", "sfkv_cache_layout",
     "sfkv_linear_bytes", "sfkv_linear_init", "sfkv_linear_destroy",
     "sfkv_linear_calibrate_scales", "sfkv_linear_write", "sfkv_linear_workspace_bytes",
@@ -77,6 +77,7 @@ _sig("sfkv_calibrate_scales", ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i32, _
 _sig("sfkv_cache_write", ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i32, _vp)
 _sig("sfkv_attend_workspace_bytes", _sz, _vp)
 _sig("sfkv_attend", ctypes.c_int, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
+_sig("sfkv_write_attend", ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
 _sig("sfkv_rebase_positions", ctypes.c_int, _vp, _i64, _vp)
 _sig("sfkv_cache_state", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i32), _P(_i32))
 _sig("sfkv_cache_layout", ctypes.c_int, _vp, _P(_sz), _P(_sz), _P(_sz), _P(_sz))
@@ -167,6 +168,19 @@ def attend(handle: int, q: torch.Tensor, out: torch.Tensor, workspace: Optional[
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.sfkv_attend(handle, q.data_ptr(), _dtype_code(q), q.shape[0], out.data_ptr(),
                             ws_ptr, ws_len, _stream(stream)))
+
+
+def write_attend(handle: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    code = _dtype_code(k)
+    if _dtype_code(v) != code or _dtype_code(q) != code:
+        raise ValueError("k, v and q must share one dtype")
+    if v.shape != k.shape or q.shape != k.shape:
+        raise ValueError("k, v and q must have one shape [n, heads, head_dim]")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.sfkv_write_attend(handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), code, k.shape[0],
+                                  out.data_ptr(), ws_ptr, ws_len, _stream(stream)))
 
 
 def rebase_positions(handle: int, delta: int, stream=None):
@@ -284,6 +298,17 @@ class RingCache:
         if workspace is None:
             workspace = torch.empty(self.workspace_bytes(), dtype=torch.uint8, device=q.device)
         attend(self.handle, q, out, workspace, stream)
+        return out
+
+    def write_attend(self, k, v, q, out=None, workspace=None, stream=None):
+        """cache_write(k, v) then attend(q) in one call (one launch fewer)."""
+        H, d = self.cfg.num_heads, self.cfg.head_dim
+        k, v, q = _frame(k, H, d), _frame(v, H, d), _frame(q, H, d)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes(), dtype=torch.uint8, device=q.device)
+        write_attend(self.handle, k, v, q, out, workspace, stream)
         return out
 
     def rebase_positions(self, delta: int, stream=None):

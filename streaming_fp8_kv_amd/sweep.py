@@ -12,7 +12,8 @@ Inputs are drawn on the device from per-cache seeded generators (seed
 default, or bf16). Every cache is calibrated on its first frame and prefilled with
 ``spec.prefill_frames`` frames, so the ring has wrapped before the first timed
 step. A timed step writes each cache's step frame at the next positions and
-attends its queries over the whole ring.
+attends its queries over the whole ring, by default through the fused
+write + attend call.
 """
 from __future__ import annotations
 
@@ -66,11 +67,15 @@ class Sweep:
         st = self.caches[0].state()
         return (self.rope.max_position - st["next_pos"]) // self.n
 
-    def step(self, stream=None):
-        """One diffusion step: write + attend on every cache, in order."""
+    def step(self, stream=None, fused: bool = True):
+        """One diffusion step: write + attend on every cache, in order, as one
+        fused call per cache (or, with fused=False, cache_write then attend)."""
         for c, (q, k, v), out in zip(self.caches, self.frames, self.outs):
-            c.cache_write(k, v, stream)
-            self.sfkv.attend(c.handle, q, out, self.workspace, stream)
+            if fused:
+                self.sfkv.write_attend(c.handle, k, v, q, out, self.workspace, stream)
+            else:
+                c.cache_write(k, v, stream)
+                self.sfkv.attend(c.handle, q, out, self.workspace, stream)
 
     def reset_all(self, stream=None):
         """Position reset of every cache: one delta rotation each (to position 0)."""

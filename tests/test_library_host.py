@@ -111,6 +111,7 @@ def test_null_handles(sfkv):
     assert lib.sfkv_cache_write(None, 256, 256, 0, 1, None) == sfkv.EINVAL
     assert lib.sfkv_calibrate_scales(None, 256, 256, 0, 1, None) == sfkv.EINVAL
     assert lib.sfkv_attend(None, 256, 0, 1, 256, None, 0, None) == sfkv.EINVAL
+    assert lib.sfkv_write_attend(None, 256, 256, 256, 0, 1, 256, None, 0, None) == sfkv.EINVAL
     assert lib.sfkv_rebase_positions(None, 0, None) == sfkv.EINVAL
     assert lib.sfkv_cache_state(None, None, None, None, None) == sfkv.EINVAL
     assert lib.sfkv_attend_workspace_bytes(None) == 0
