@@ -41,10 +41,12 @@ PEAK_FP8_TFLOPS = 5000.0      # dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
 
 # HBM traffic of one attend call (query prep + attention + merge), from two
-# rocprofv3 --pmc passes over this benchmark (FETCH_SIZE scaled by 2.0335,
-# WRITE_SIZE as counted; the calibration is in the traffic profile). None
-# whenever the attend kernels have changed since the counters were taken.
-ATTEND_TRAFFIC_BYTES = None
+# rocprofv3 --pmc passes over this benchmark: FETCH_SIZE scaled by 2.0335 (a
+# plain copy kernel of 17.78 MB read reads 8,538.8 KiB of FETCH_SIZE) and
+# WRITE_SIZE as counted (the same copy's 17.78 MB write reads 17,363.3 KiB):
+# fetch 5.57 + 61.69 + 21.10 MB, write 7.27 + 17.06 + 9.30 MB. Set to None
+# whenever the attend kernels change until the counters are taken again.
+ATTEND_TRAFFIC_BYTES = 121.98e6
 
 
 def parse():
