@@ -1,7 +1,8 @@
 """Build libsfkv.so for gfx950 in-tree with hipcc.
 
 Usage: ``python -m streaming_fp8_kv_amd.build`` (or ``build()`` from Python).
-Always recompiles every source.
+Always recompiles every source. Also builds ``tests/c_abi/session``, a plain C
+program that drives the library through its C ABI (the GPU tests run it).
 """
 from __future__ import annotations
 
@@ -60,7 +61,25 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    _build_c_session(verbose)
     return LIB
+
+
+def _build_c_session(verbose: bool) -> str:
+    """The C consumer of the ABI: gcc, C11, linked against the in-tree library
+    and the HIP runtime (for hipMalloc and copies only)."""
+    src = os.path.join(ROOT, "tests", "c_abi", "session.c")
+    exe = os.path.join(ROOT, "tests", "c_abi", "session")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    msgs = _run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+                 "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
+                 src, "-o", exe + ".tmp",
+                 "-L", PKG, "-lsfkv", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+                 "-Wl,-rpath,$ORIGIN/../../streaming_fp8_kv_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")])
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(exe + ".tmp", exe)
+    return exe
 
 
 if __name__ == "__main__":

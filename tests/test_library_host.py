@@ -127,3 +127,14 @@ def test_binding_has_no_fallback():
     src = open(os.path.join(ROOT, "streaming_fp8_kv_amd", "sfkv.py")).read()
     assert "import oracle" not in src and "from oracle" not in src
     assert "raise ImportError" in src
+
+
+def test_c_session_usage():
+    """The C consumer of the ABI links against the library and rejects a bad
+    command line before touching the GPU."""
+    import subprocess
+    exe = os.path.join(ROOT, "tests", "c_abi", "session")
+    if not os.path.exists(exe):
+        pytest.skip("tests/c_abi/session not built")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
