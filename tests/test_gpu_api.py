@@ -127,11 +127,14 @@ def test_encoder_boundaries_through_write(sfkv, rope128):
     assert np.array_equal(c.k_codes()[0, :n].cpu().numpy(), ora.k[0, :n])
 
 
-def test_graph_captured_chain_matches_eager(sfkv):
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_captured_chain_matches_eager(sfkv, fused):
     """write -> attend -> write -> attend ... captured once into a graph and
     replayed; every replay must reproduce the eager run bit for bit, with eager
-    work between replays (the chained-call tests the pages describe)."""
-    say("case graph-captured chain")
+    work between replays (the chained-call tests the pages describe). With
+    fused=True the graph holds sfkv_write_attend calls, checked against eager
+    separate calls."""
+    say(f"case graph-captured chain (fused={fused})")
     spec = W.PROD
     s = spec.shape
     rope = sfkv.Rope(s.head_dim, 16384)
@@ -161,8 +164,11 @@ def test_graph_captured_chain_matches_eager(sfkv):
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
             for (q, k, v), o in zip(frames[3:], g_outs):
-                g_cache.cache_write(k, v)
-                g_cache.attend(q, out=o, workspace=ws)
+                if fused:
+                    g_cache.write_attend(k, v, q, out=o, workspace=ws)
+                else:
+                    g_cache.cache_write(k, v)
+                    g_cache.attend(q, out=o, workspace=ws)
     torch.cuda.synchronize()
     for rep in range(3):
         for o in g_outs:
@@ -180,8 +186,9 @@ def test_graph_captured_chain_matches_eager(sfkv):
 
 def test_no_host_synchronisation_in_step(sfkv):
     """With the stream held busy by a long device-side sleep, a full 24-call slice
-    of the step (write + attend) and a reset must all return on the host while the
-    GPU is still asleep: no call waits for the device."""
+    of the step (write + attend, half of the calls through the fused entry point)
+    and a reset must all return on the host while the GPU is still asleep: no
+    call waits for the device."""
     say("case no host sync")
     spec = W.PROD
     s = spec.shape
@@ -200,10 +207,13 @@ def test_no_host_synchronisation_in_step(sfkv):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     torch.cuda._sleep(int(3e8))              # a bounded device-side spin (0.1 s or more)
-    for c, (q, k, v), o in zip(caches, frames, outs):
+    for i, (c, (q, k, v), o) in enumerate(zip(caches, frames, outs)):
         c.rebase_positions(c.state()["next_pos"])
-        c.cache_write(k, v)
-        c.attend(q, out=o, workspace=ws)
+        if i % 2:
+            c.write_attend(k, v, q, out=o, workspace=ws)
+        else:
+            c.cache_write(k, v)
+            c.attend(q, out=o, workspace=ws)
     still_busy = not stream.query()
     torch.cuda.synchronize()
     assert still_busy, "the host waited for the device during the step"
