@@ -117,8 +117,10 @@ void sfkv_cache_destroy(sfkv_cache *cache);
  * computed on the device and kept there (no host readback): absmax over the
  * frame of the keys rotated at the positions the next write will use, and of
  * the raw values; scale = absmax/448 and inv = 448/absmax, divided in fp64 and
- * rounded once to fp32 (1 and 1 for an all-zero head). Does not advance the
- * ring. May be called again to re-calibrate.
+ * rounded once to fp32 (1 and 1 for an all-zero head). With bf16 storage the
+ * pair is instead 2^e and 2^-e with absmax in [256, 512) * 2^e (see
+ * sfkv_storage). Does not advance the ring. May be called again to
+ * re-calibrate.
  * Errors: EINVAL (pointers, dtype, n_tokens outside [1, max_new_tokens]),
  *         ERANGE (the frame's positions would reach max_position).
  * Source: "Do It Once, at Write Time" (per-head scales calibrated once per
@@ -129,7 +131,8 @@ sfkv_status sfkv_calibrate_scales(sfkv_cache *cache, const void *k, const void *
 /* sfkv_cache_write: append one frame. Token i (0-based) goes to slot
  * (write_slot + i) mod capacity at position next_pos + i; its key is rotated
  * at that position and both key and value are quantised with the head's
- * scale; positions[slot] is set. Then tokens += n, next_pos += n.
+ * scale (E4M3 storage) or rounded to bf16 (bf16 storage); positions[slot] is
+ * set. Then tokens += n, next_pos += n.
  * Errors: EINVAL (pointers, dtype, n_tokens outside [1, max_new_tokens]),
  *         ESTATE (no calibration yet),
  *         ERANGE (next_pos + n_tokens > max_position of the rope table).
@@ -141,8 +144,9 @@ sfkv_status sfkv_cache_write(sfkv_cache *cache, const void *k, const void *v,
  * head, with no mask. q [n_q][H][d] are the queries of the most recent write
  * (n_q must equal that write's n_tokens); they are rotated at that write's
  * positions inside the kernel. Keys and values are the decoded FP8 codes times
- * the head's scale. Slot order does not matter because every key carries its
- * own rotation. Output is fp32 [n_q][H][d].
+ * the head's scale (E4M3 storage) or the stored bf16 values (bf16 storage).
+ * Slot order does not matter because every key carries its own rotation.
+ * Output is fp32 [n_q][H][d].
  * `workspace` is device memory (256-byte aligned) of at least
  * sfkv_attend_workspace_bytes(cache) bytes; it holds the prepared query terms
  * and split partials of one call. The size depends only on the cache
@@ -176,7 +180,8 @@ sfkv_status sfkv_write_attend(sfkv_cache *cache, const void *k, const void *v, c
 /* sfkv_rebase_positions: subtract delta from every position with one delta
  * rotation of the cached keys: each valid key's FP8 codes are rotated by
  * -delta*theta in the code domain (the per-head scale cancels), clamped and
- * re-encoded; values are untouched; positions[slot] -= delta for valid slots;
+ * re-encoded (bf16 storage: decoded exactly, rotated in fp32, rounded to
+ * bf16); values are untouched; positions[slot] -= delta for valid slots;
  * next_pos -= delta; the last write's query positions move by -delta too, so
  * attention is unchanged up to rounding. Resetting positions to 0 is
  * delta = next_pos.

@@ -8,7 +8,8 @@
 // rotated here, at the positions of the write they belong to.
 //
 // Data path per workgroup (one head, 128 queries = 4 waves x 32, one key range):
-//   * queries (a small kernel of their own, once per call): bf16 -> fp32 RoPE ->
+//   * queries (once per call, in a small kernel of their own or inside the
+//     write's launch of the fused call): bf16 -> fp32 RoPE ->
 //     times scale_k * log2(e) / sqrt(d) -> three E4M3 terms, each with one
 //     power-of-two (E8M0) scale per 32 head dims; each wave keeps its 32
 //     queries' terms in registers as the B operand of the block-scaled FP8
@@ -30,7 +31,7 @@
 // runs at half rate).
 //
 // Long key ranges are split across workgroups (split-KV) to fill the 256 CUs; a
-// second kernel merges the partial (max, sum, O) triples.
+// second kernel merges the partial (max, sum, O / sum) triples, O / sum in fp16.
 #include "query_prep.h"
 #include "sfkv_internal.h"
 
