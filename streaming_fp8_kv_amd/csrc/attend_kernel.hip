@@ -35,7 +35,6 @@
 #include "query_prep.h"
 #include "sfkv_internal.h"
 
-#include <cstdlib>
 
 namespace sfkv {
 namespace {
@@ -656,7 +655,6 @@ AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus) {
   const int64_t nt = (n_valid + BK - 1) / BK;
   const int64_t max_split = nt / 4 > 1 ? nt / 4 : 1;
   int64_t g = 2 * static_cast<int64_t>(cus > 0 ? cus : 256);
-  if (const char *env = getenv("SFKV_ATTEND_WORKERS")) g = atoi(env);
   if (g > pairs * max_split) g = pairs * max_split;
   if (g < pairs) g = pairs;
   AttendPlan p;
