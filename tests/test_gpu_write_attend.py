@@ -107,3 +107,35 @@ def test_fused_errors_leave_state(sfkv):
     assert st == sfkv.EINVAL and c.state() == before
     torch.cuda.synchronize()
     assert int(c.positions().abs().sum()) == 0
+
+
+@pytest.mark.parametrize("storage", ["fp8", "bf16"])
+def test_fused_long_session_with_resets(sfkv, storage):
+    """The 200-step session with a reset to position 0 every 42 steps, every
+    step through the fused call; three heads mirrored, attention checked around
+    every reset."""
+    spec = W.LONG
+    heads = [0, 11, 23]
+    say(f"case write_attend long session {storage}")
+    rope = sfkv.Rope(spec.shape.head_dim, spec.shape.max_position, spec.shape.rope_base)
+    m = Mirror(sfkv, rope, spec, heads=heads, storage=storage)
+    fs = W.FrameStream(spec)
+    ws = torch.empty(m.gpu.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    check = {0, 41, 42, 43, 84, 126, 168, 199}
+    for step in range(spec.steps):
+        q, k, v = fs.frame()
+        if step == 0:
+            m.calibrate(k, v)
+        if step > 0 and step % spec.reset_period == 0:
+            m.rebase(m.ora.next_pos)
+        out = m.gpu.write_attend(k.cuda(), v.cuda(), q.cuda(), workspace=ws)
+        m.ora.write(m._sub(k), m._sub(v))
+        if step in check:
+            m.check_cache(f"step {step}")
+            torch.cuda.synchronize()
+            rows = spread_rows(q.shape[0], 48)
+            got = out[torch.as_tensor(rows)][:, heads].cpu().numpy()
+            ref = m.reference_from_gpu_cache(q, rows)
+            a_err, b_err = attention_error(got, ref)
+            say(f"  step {step}: A={a_err:.2e} B={b_err:.2e}")
+            assert a_err <= A_MAX and b_err <= B_MEAN
