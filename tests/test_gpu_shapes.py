@@ -87,3 +87,34 @@ def test_large_ring_sampled(sfkv):
     assert st["n_valid"] == cap and st["write_slot"] == (6 * n) % cap
     m.check_cache("after 6 writes")
     m.check_attend(q, rows=spread_rows(n, 24), tag="last write")
+
+
+@pytest.mark.parametrize("storage", ["fp8", "bf16"])
+def test_degenerate_heads(sfkv, storage):
+    """Head 0 all zeros (scale 1, every score 0, uniform weights over zero
+    values: output exactly 0), head 1 with the same raw key at every position
+    and one constant value (whatever the weights, the output is that value),
+    head 2 ordinary; four writes that wrap a 96-slot ring, checked in full
+    against the oracle."""
+    heads, d, cap, n = 3, 64, 96, 40
+    shape = W.CacheShape(heads, d, cap, n, max_position=4096)
+    spec = W.WorkloadSpec(name="degenerate", shape=shape, seed=51, dtype=torch.float32, dist="normal",
+                          sigma_q=None, sigma_kv=None, steps=4)
+    say(f"case degenerate heads {storage}")
+    rope = sfkv.Rope(d, shape.max_position)
+    m = Mirror(sfkv, rope, spec, storage=storage)
+    fs = W.FrameStream(spec)
+    key = torch.linspace(-1.5, 1.5, d)
+    for step in range(spec.steps):
+        q, k, v = fs.frame()
+        q[:, 0], k[:, 0], v[:, 0] = 0.0, 0.0, 0.0
+        k[:, 1] = key                    # the same raw key at every position (rotated differently)
+        v[:, 1] = 0.75
+        if step == 0:
+            m.calibrate(k, v)
+        m.write(k, v)
+        m.check_cache(f"step {step}")
+        out = m.check_attend(q, tag=f"step {step}")
+        o = out.cpu()
+        assert torch.all(o[:, 0] == 0.0), "an all-zero head must attend to zeros"
+        assert torch.allclose(o[:, 1], torch.full_like(o[:, 1], 0.75), rtol=0, atol=1e-6)
