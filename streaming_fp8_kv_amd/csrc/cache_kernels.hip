@@ -180,30 +180,31 @@ __device__ inline float wave_max(float m) {
 
 // One block per (head, tensor): absmax of the rotated keys (blockIdx.y == 0)
 // or of the raw values (blockIdx.y == 1) over the frame, then the two scales.
-// The maximum is exact and order-free, so the result is deterministic.
-__global__ __launch_bounds__(256) void calibrate_kernel(CalibrateLaunch a) {
+// A thread takes 8 dims of one token per step (one 16- or 32-byte load; keys
+// rotated pair by pair as the write rotates them). The maximum is exact and
+// order-free, so the result is deterministic.
+constexpr int kCalibrateThreads = 1024;
+__global__ __launch_bounds__(kCalibrateThreads) void calibrate_kernel(CalibrateLaunch a) {
   const int h = blockIdx.x;
   const bool keys = blockIdx.y == 0;
-  const int pairs = a.head_dim >> 1;
+  const int groups = a.head_dim >> 3;           // 8-dim groups per (token, head)
   const void *src = keys ? a.k : a.v;
   float m = 0.0f;
-  const int total = a.n * pairs;
+  const int total = a.n * groups;
   for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int i = e / pairs, pr = e - i * pairs;
-    const size_t elem = (static_cast<size_t>(i) * a.heads + h) * a.head_dim + 2 * pr;
-    float x0, x1;
-    if (a.dtype == 0) {
-      uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(src) + elem);
-      x0 = bf16_lo(w); x1 = bf16_hi(w);
-    } else {
-      float2 w = *reinterpret_cast<const float2 *>(static_cast<const float *>(src) + elem);
-      x0 = w.x; x1 = w.y;
+    const int i = e / groups, g = e - i * groups;
+    float x[8];
+    load8(src, (static_cast<size_t>(i) * a.heads + h) * a.head_dim + 8 * g, a.dtype, x);
+    if (keys) {
+      const RopePair *row = a.rope + static_cast<size_t>(a.pos0 + i) * (a.head_dim >> 1) + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rotate_pair(x[2 * j], x[2 * j + 1], row[j]);
     }
-    if (keys) rotate_pair(x0, x1, a.rope[static_cast<size_t>(a.pos0 + i) * pairs + pr]);
-    m = fmaxf(m, fmaxf(fabsf(x0), fabsf(x1)));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
   }
   m = wave_max(m);
-  __shared__ float partial[4];
+  __shared__ float partial[kCalibrateThreads / 64];
   if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -355,7 +356,7 @@ hipError_t launch_shift(const ShiftLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s) {
-  hipLaunchKernelGGL(calibrate_kernel, dim3(a.heads, 2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(calibrate_kernel, dim3(a.heads, 2), dim3(kCalibrateThreads), 0, s, a);
   return hipGetLastError();
 }
 
