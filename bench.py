@@ -14,9 +14,10 @@ point (the write's launch also prepares the frame's queries; same bits as the
 two separate calls). The same step as separate cache_write and attend calls is
 timed next (``unfused_*``). ``roofline`` is for attend, the dominant call:
 algorithmic FLOPs per call (4 * n * slots * heads * head_dim) over its average
-duration from HIP events recorded around each of one step's 240 separate
-attend calls, on the stream the kernels run on, against the dense FP8 MFMA
-peak. One separate attend call is three kernel launches (query prep,
+duration, from two HIP events around one pass of 240 attend calls issued back
+to back (each over its own cold ring), on the stream the kernels run on,
+against the dense FP8 MFMA peak; events around each single call
+(``attend_us_with_events``) add their own few microseconds. One separate attend call is three kernel launches (query prep,
 attention, split combine); the rocprofv3 summary lists each. cache_write
 alone, the fused step captured once as a HIP graph and replayed, and the
 position reset (one delta rotation per cache) are timed in separate regions
@@ -102,8 +103,9 @@ def cpu_baseline(n_calls: int):
 def plain_path(sfkv, W, spec, n_caches: int, stream):
     """The launch software's cache on `n_caches` caches of the production shape:
     each window is filled with 8 frames, then one write (copy-shift + rotate and
-    re-quantise the whole window) and one attend per cache are timed with events
-    around each call. Inputs are drawn on the device before timing."""
+    re-quantise the whole window) per cache is timed as one back-to-back pass,
+    and one attend per cache as another. Inputs are drawn on the device before
+    timing."""
     import torch
     s = spec.shape
     E = torch.cuda.Event
@@ -124,17 +126,20 @@ def plain_path(sfkv, W, spec, n_caches: int, stream):
     for c, (q, k, v) in zip(caches, last):          # warm-up: one steady-state call each
         c.cache_write(k, v, stream)
         c.attend(q, out, ws, stream)
-    ev = [(E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)) for _ in caches]
+    # one pass of writes, then one pass of attends, each back to back between
+    # two events (each attend uses its own cache's write)
+    e0, e1, e2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
-    for c, (q, k, v), (a, b, e) in zip(caches, last, ev):
-        a.record(stream)
+    e0.record(stream)
+    for c, (q, k, v) in zip(caches, last):
         c.cache_write(k, v, stream)
-        b.record(stream)
+    e1.record(stream)
+    for c, (q, k, v) in zip(caches, last):
         c.attend(q, out, ws, stream)
-        e.record(stream)
+    e2.record(stream)
     torch.cuda.synchronize()
-    upkeep = sum(a.elapsed_time(b) for a, b, _ in ev) * 1e3 / len(ev)
-    attend = sum(b.elapsed_time(e) for _, b, e in ev) * 1e3 / len(ev)
+    upkeep = e0.elapsed_time(e1) * 1e3 / len(caches)
+    attend = e1.elapsed_time(e2) * 1e3 / len(caches)
     del caches
     return {"upkeep_us": upkeep, "attend_us": attend}
 
@@ -142,7 +147,7 @@ def plain_path(sfkv, W, spec, n_caches: int, stream):
 def bf16_sweep(sfkv, W, spec, n_calls: int, steps: int, stream):
     """The same 240-call step over caches that store bf16 instead of E4M3 (the
     non-FP8 variant): two untimed steps, `steps` timed fused steps, then one
-    step of separate calls with events around every attend call."""
+    back-to-back pass of attend calls between two events."""
     import torch
     from streaming_fp8_kv_amd.sweep import Sweep
     E = torch.cuda.Event
@@ -158,14 +163,14 @@ def bf16_sweep(sfkv, W, spec, n_calls: int, steps: int, stream):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
-    att = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
-    for (c, (q, k, v), out), (a0, a1) in zip(zip(sw.caches, sw.frames, sw.outs), att):
-        sfkv.cache_write(c.handle, k, v, stream)
-        a0.record(stream)
-        sfkv.attend(c.handle, q, out, sw.workspace, stream)
-        a1.record(stream)
+    a0, a1 = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
-    attend_us = sum(a.elapsed_time(b) for a, b in att) * 1e3 / len(att)
+    a0.record(stream)
+    for c, (q, k, v), out in zip(sw.caches, sw.frames, sw.outs):
+        sfkv.attend(c.handle, q, out, sw.workspace, stream)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    attend_us = a0.elapsed_time(a1) * 1e3 / n_calls
     del sw
     return {"ms_per_step": ms, "attend_us": attend_us}
 
@@ -187,7 +192,7 @@ def main():
     sw = Sweep(sfkv, n_caches=n_calls, spec=spec)
     sw.prefill()
     torch.cuda.synchronize()
-    if sw.positions_left() < args.warmup + args.steps + 5:
+    if sw.positions_left() < args.warmup + args.steps + 6:
         raise SystemExit("too many steps for the position range; lower --steps/--warmup")
 
     stream = torch.cuda.current_stream()
@@ -226,17 +231,30 @@ def main():
         sfkv.attend(c.handle, q, out, sw.workspace, stream)
         a1.record(stream)
     torch.cuda.synchronize()
-    attend_us = sum(a.elapsed_time(b) for a, b in att) * 1e3 / len(att)
+    attend_us_events = sum(a.elapsed_time(b) for a, b in att) * 1e3 / len(att)
 
-    # ---- cache_write alone, one step's worth, events around every launch ----
-    wr = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
+    # ---- the attend call's duration for the roofline: one pass of 240 attend
+    # calls back to back (each cache's last write's queries over its own cold
+    # ring), two events around the pass, so no per-call event sits between the
+    # launches ----
+    p0, p1 = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
-    for c, (q, k, v), (a, b) in zip(sw.caches, sw.frames, wr):
-        a.record(stream)
+    p0.record(stream)
+    for c, (q, k, v), out in zip(sw.caches, sw.frames, sw.outs):
+        sfkv.attend(c.handle, q, out, sw.workspace, stream)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    attend_us = p0.elapsed_time(p1) * 1e3 / n_calls
+
+    # ---- cache_write alone: one step's worth back to back between two events ----
+    w0, w1 = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    w0.record(stream)
+    for c, (q, k, v) in zip(sw.caches, sw.frames):
         sfkv.cache_write(c.handle, k, v, stream)
-        b.record(stream)
+    w1.record(stream)
     torch.cuda.synchronize()
-    write_us = sum(a.elapsed_time(b) for a, b in wr) * 1e3 / len(wr)
+    write_us = w0.elapsed_time(w1) * 1e3 / n_calls
 
     # ---- the same step captured once as a HIP graph and replayed -----------
     # (the capture enqueues one step's 480 launches; replays repeat it with the
@@ -259,15 +277,16 @@ def main():
     graph_ms = g0.elapsed_time(g1) / args.steps
     del graph
 
-    # ---- position reset: one delta rotation of every cache ------------------
-    rb = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n_calls)]
+    # ---- position reset: one delta rotation of every cache, back to back
+    # between two events ----
+    r0, r1 = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
-    for c, (a, b) in zip(sw.caches, rb):
-        a.record(stream)
+    r0.record(stream)
+    for c in sw.caches:
         c.rebase_positions(c.state()["next_pos"], stream)
-        b.record(stream)
+    r1.record(stream)
     torch.cuda.synchronize()
-    rebase_us = sum(a.elapsed_time(b) for a, b in rb) * 1e3 / len(rb)
+    rebase_us = r0.elapsed_time(r1) * 1e3 / n_calls
 
     plain = plain_path(sfkv, W, spec, args.plain_calls, stream) if args.plain_calls > 0 else None
     if args.bf16_steps > 0:
@@ -306,6 +325,7 @@ def main():
                      "launch_us": round(attend_us, 3)},
         "extra": {
             "attend_us": round(attend_us, 3),
+            "attend_us_with_events": round(attend_us_events, 3),
             "write_us": round(write_us, 3),
             "write_hbm_frac": round(write_bytes / (write_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "rebase_us_per_cache": round(rebase_us, 3),
