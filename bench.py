@@ -42,12 +42,13 @@ PEAK_FP8_TFLOPS = 5000.0      # dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
 
 # HBM traffic of one attend call (query prep + attention + merge), from two
-# rocprofv3 --pmc passes over this benchmark: FETCH_SIZE scaled by 2.0335 (a
-# plain copy kernel of 17.78 MB read reads 8,538.8 KiB of FETCH_SIZE) and
-# WRITE_SIZE as counted (the same copy's 17.78 MB write reads 17,363.3 KiB):
-# fetch 5.57 + 61.69 + 21.10 MB, write 7.27 + 17.06 + 9.30 MB. Set to None
-# whenever the attend kernels change until the counters are taken again.
-ATTEND_TRAFFIC_BYTES = 121.98e6
+# rocprofv3 --pmc passes over this benchmark: FETCH_SIZE scaled by 1.9972 (a
+# plain scale kernel reading 17.78 MB counts 8,694.0 KiB of FETCH_SIZE; see
+# --copy-calibration) and WRITE_SIZE as counted (its 17.78 MB write counts
+# 17,363.3 KiB): fetch 5.47 + 60.59 + 20.72 MB, write 7.27 + 17.06 + 9.30 MB.
+# Set to None whenever the attend kernels change until the counters are taken
+# again.
+ATTEND_TRAFFIC_BYTES = 120.40e6
 
 
 def parse():
@@ -62,7 +63,30 @@ def parse():
                     help="timed steps of the same sweep over bf16 rings (0 skips)")
     ap.add_argument("--plain-calls", type=int, default=24,
                     help="caches for the plain-path (linear window) comparison; 0 skips it")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain fp32 scale kernels of known traffic (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """Plain fp32 scale kernels (torch.mul) whose HBM traffic is known: each
+    launch reads and writes the stated bytes once. Under ``rocprofv3 --pmc
+    FETCH_SIZE`` (or WRITE_SIZE) the ratio of these bytes to the counted KiB per
+    dispatch is the factor that turns the counter into bytes. Prints one line
+    per size."""
+    import torch
+    torch.cuda.set_device(0)
+    for mb in (13.95, 35.56, 64.0, 512.0):
+        n = int(mb * 1e6 / 8)                      # half the traffic read, half written
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(8):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"elements": n, "bytes_read": 4 * n, "bytes_written": 4 * n,
+                                               "launches": 8}}), flush=True)
+        del a, b
 
 
 def cpu_baseline(n_calls: int):
@@ -180,6 +204,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from streaming_fp8_kv_amd import sfkv, workloads as W
     from streaming_fp8_kv_amd.sweep import Sweep
