@@ -202,7 +202,7 @@ def bf16_sweep(sfkv, W, spec, n_calls: int, steps: int, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
