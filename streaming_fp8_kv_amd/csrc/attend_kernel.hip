@@ -409,6 +409,13 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
   };
+  // Two weights of a block as one packed fp16 pair, added to the row sum.
+  auto exp2p = [&](const v16f &s, int i0, uint32_t *w) {
+    const v2h a = __builtin_convertvector(
+        (float2_t){__builtin_amdgcn_exp2f(s[i0] - m_ref), __builtin_amdgcn_exp2f(s[i0 + 1] - m_ref)}, v2h);
+    w[0] = __builtin_bit_cast(uint32_t, a);
+    add_pair(w[0]);
+  };
   // Four weights of a block as two packed fp16 pairs, added to the row sum.
   auto exp4 = [&](const v16f &s, int i0, uint32_t *w) {
     const v2h a = __builtin_convertvector(
@@ -451,10 +458,21 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
       if constexpr (BF) qk_step_bf(kfb, i, s_next);
       else qk_step(kf, i, s_next);
       if (load && i == 0) load_tile(kt_load);
-      if (i < 4) exp4(s_cur, 4 * i, pw + 2 * i);
-      if (i == NQK - 1) {
+      if constexpr (NQK == 6) {
+        // the eight weight pairs spread over all six score MFMAs, 2,1,2,1,1,1
+        // (measured 1.6% faster per attend call than four groups of four
+        // after the first four: no group outlasts the MFMA it hides behind)
+        constexpr int first[7] = {0, 2, 3, 5, 6, 7, 8};
 #pragma unroll
-        for (int g = NQK; g < 4; ++g) exp4(s_cur, 4 * g, pw + 2 * g);
+        for (int pr = first[i]; pr < first[i + 1]; ++pr) exp2p(s_cur, 2 * pr, pw + pr);
+      } else {
+        if (i < 4) exp4(s_cur, 4 * i, pw + 2 * i);
+      }
+      if (i == NQK - 1) {
+        if constexpr (NQK != 6) {
+#pragma unroll
+          for (int g = NQK; g < 4; ++g) exp4(s_cur, 4 * g, pw + 2 * g);
+        }
         if (stage) store_k(sbuf);
       }
       __builtin_amdgcn_sched_barrier(0);
