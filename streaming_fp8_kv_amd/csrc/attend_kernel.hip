@@ -224,6 +224,7 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
   // past the range read as zeros without touching memory; the per-thread offset
   // is fixed and the tile start is the scalar offset.
   constexpr int KPASS = (BK * D * ES / 16) / 256;
+  static_assert(!(BF && D == 128) || KPASS == 4, "the bf16 staging spread places four K chunks per thread");
   constexpr int KCH = D * ES / 16;         // 16-byte chunks per key row
   constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor, gfx9 family
   const int v_dg = tid & 15, v_kq = tid >> 4;
@@ -266,12 +267,13 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
   // Staging of a loaded tile into LDS buffer buf, in parts so that the pieces
   // can sit between matrix instructions: K rows as they are, V widened to fp16
   // (exact: E4M3 is a subset of fp16), one 16-byte chunk of one key per store.
+  auto store_k1 = [&](int buf, int p) {
+    const int c = tid + p * 256, key = c / KCH, col = c % KCH;
+    *reinterpret_cast<uint4 *>(sK[buf] + key * KROW + 16 * col) = pk[p];
+  };
   auto store_k = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int c = tid + p * 256, key = c / KCH, col = c % KCH;
-      *reinterpret_cast<uint4 *>(sK[buf] + key * KROW + 16 * col) = pk[p];
-    }
+    for (int p = 0; p < KPASS; ++p) store_k1(buf, p);
   };
   // row 4 v_kq + j has (row & 3) == j; the fp8 -> fp16 widening happens right
   // before the store, so only the loaded codes stay live between the phases
@@ -466,10 +468,15 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
 #pragma unroll
         for (int pr = first[i]; pr < first[i + 1]; ++pr) exp2p(s_cur, 2 * pr, pw + pr);
       } else if constexpr (NQK == 16) {
-        // bf16 keys at d = 128: one weight pair behind every other score
-        // MFMA (2.5% faster per bf16 attend call than four groups of four
-        // behind the first four)
+        // bf16 keys at d = 128 (one wave per SIMD, so the vector work has only
+        // this wave's MFMAs to hide behind): one weight pair behind every even
+        // score MFMA (2.5% faster per bf16 attend call than four groups of
+        // four behind the first four), and the staging of the next tile
+        // behind the odd ones, V rows behind 1, 3, 5, 7 and K chunks behind
+        // 9, 11, 13, 15 (2.2% faster than after the score and P V MFMAs)
         if (i % 2 == 0) exp2p(s_cur, i, pw + i / 2);
+        if (stage && i % 2 == 1 && i < 8) store_v(sbuf, i / 2);
+        if (stage && i % 2 == 1 && i >= 8) store_k1(sbuf, (i - 8) / 2);
       } else {
         if (i < 4) exp4(s_cur, 4 * i, pw + 2 * i);
       }
@@ -478,7 +485,9 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
 #pragma unroll
           for (int g = NQK; g < 4; ++g) exp4(s_cur, 4 * g, pw + 2 * g);
         }
-        if (stage) store_k(sbuf);
+        if constexpr (NQK != 16) {
+          if (stage) store_k(sbuf);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -491,13 +500,13 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db], pb0, oacc[db], 0, 0, 0);
-      if (stage && db < 4) store_v(sbuf, db);
+      if (NQK != 16 && stage && db < 4) store_v(sbuf, db);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db], pb1, oacc[db], 0, 0, 0);
-      if (stage && NDB + db < 4) store_v(sbuf, NDB + db);
+      if (NQK != 16 && stage && NDB + db < 4) store_v(sbuf, NDB + db);
       if (db == NDB - 1) tmax_next = block_max(s_next);   // in the shadow of the PV MFMAs
       __builtin_amdgcn_sched_barrier(0);
     }
