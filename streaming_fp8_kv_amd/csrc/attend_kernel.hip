@@ -267,13 +267,17 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
   // Staging of a loaded tile into LDS buffer buf, in parts so that the pieces
   // can sit between matrix instructions: K rows as they are, V widened to fp16
   // (exact: E4M3 is a subset of fp16), one 16-byte chunk of one key per store.
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) {
+      const int c = tid + p * 256, key = c / KCH, col = c % KCH;
+      *reinterpret_cast<uint4 *>(sK[buf] + key * KROW + 16 * col) = pk[p];
+    }
+  };
+  // one chunk of the same (the bf16 loop spreads them over its MFMAs)
   auto store_k1 = [&](int buf, int p) {
     const int c = tid + p * 256, key = c / KCH, col = c % KCH;
     *reinterpret_cast<uint4 *>(sK[buf] + key * KROW + 16 * col) = pk[p];
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < KPASS; ++p) store_k1(buf, p);
   };
   // row 4 v_kq + j has (row & 3) == j; the fp8 -> fp16 widening happens right
   // before the store, so only the loaded codes stay live between the phases
