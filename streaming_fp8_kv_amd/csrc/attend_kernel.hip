@@ -135,6 +135,23 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// Plan pair q (small pairs 0 .. X-1 split s_lo + 1 ways, big ones s_lo
+// ways) -> the (head, query tile) pair it computes. Each XCD's share owns the
+// plan pairs whose first range it holds; they map onto one contiguous run of
+// real pairs, numbered head-major, so an XCD's pairs cover whole heads where
+// the counts allow and each head's keys and values are fetched into one L2.
+__device__ inline int real_pair(int q, int n_pairs, int slo, int X) {
+  const int NB = (n_pairs - X) * slo, NS = X * (slo + 1);
+  const int first = q < X ? q * (slo + 1) : (q - X) * slo;   // its first range in its share space
+  int x = 0;
+  for (int y = 1; y < 8; ++y)
+    if ((q < X ? NS * y / 8 : NB * y / 8) <= first) x = y;
+  const int pb0 = (NB * x / 8 + slo - 1) / slo;
+  const int ps0 = (NS * x / 8 + slo) / (slo + 1), ps1 = (NS * (x + 1) / 8 + slo) / (slo + 1);
+  const int base = ps0 + pb0;                                // pairs owned by earlier XCDs
+  return q < X ? base + (q - ps0) : base + (ps1 - ps0) + (q - X - pb0);
+}
+
 // One wave = one block of 32 queries, 4 waves per workgroup; a tile is 64 keys
 // = two blocks of 32. The loop is software-pipelined by block: the QK MFMAs of
 // the next block are issued before the softmax of the current one, so the
@@ -195,8 +212,9 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
     split = sm % (slo + 1);
     nsplit = slo + 1;
   }
-  const int h = pair / tiles_q;
-  const int qtile = pair % tiles_q;
+  const int rp = real_pair(pair, n_pairs, slo, X);
+  const int h = rp / tiles_q;
+  const int qtile = rp % tiles_q;
   const int slot = pair * slo + min(pair, X) + split;   // partial slot of this range
 
   const int tid = threadIdx.x;
@@ -645,8 +663,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
   if (k < nbig) pair = X + pb0 + k;
   else if (k < nbig + nsmall) pair = ps0 + (k - nbig);
   else return;
-  const int h = pair / tiles_q;
-  const int qi = (pair % tiles_q) * BQB + chunk * RPB + static_cast<int>(threadIdx.x) / (D / 8);
+  const int rp = real_pair(pair, n_pairs, slo, X);
+  const int h = rp / tiles_q;
+  const int qi = (rp % tiles_q) * BQB + chunk * RPB + static_cast<int>(threadIdx.x) / (D / 8);
   if (qi >= a.n_q) return;
   const int c8 = static_cast<int>(threadIdx.x) % (D / 8);
   const size_t row = static_cast<size_t>(qi) * a.heads + h;
