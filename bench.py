@@ -46,10 +46,10 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 # rocprofv3 --pmc passes over this benchmark: FETCH_SIZE scaled by 1.9972 (a
 # plain scale kernel reading 17.78 MB counts 8,694.0 KiB of FETCH_SIZE; see
 # --copy-calibration) and WRITE_SIZE as counted (its 17.78 MB write counts
-# 17,363.3 KiB): fetch 5.45 + 60.59 + 17.09 MB, write 7.27 + 17.06 + 9.30 MB.
+# 17,363.3 KiB): fetch 5.47 + 44.25 + 17.11 MB, write 7.27 + 17.07 + 9.30 MB.
 # Set to None whenever the attend kernels change until the counters are taken
 # again.
-ATTEND_TRAFFIC_BYTES = 116.76e6
+ATTEND_TRAFFIC_BYTES = 100.47e6
 
 
 def parse():

@@ -188,9 +188,10 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
   // before doubling up, in the same order). Each XCD therefore takes its share
   // of the big workgroups at local indices 0.. and its share of the small ones
   // after them, so that a big one is paired with a small one on every CU
-  // while big ones last. Consecutive workgroups of a share cover the splits
-  // and query tiles of the same heads, so a key range is fetched from HBM once
-  // into the XCD's L2 and read by every query tile of its head in step.
+  // while big ones last. The pairs an XCD's share owns are renumbered onto one
+  // contiguous run of (head, query tile) pairs (real_pair), whole heads where
+  // the counts allow, so a head's keys and values are fetched from HBM into
+  // one L2 only and read there by every query tile of the head in step.
   const int tiles_q = (a.n_q + BQB - 1) / BQB;
   const int n_pairs = tiles_q * a.heads;
   const int NT = (a.n_valid + BK - 1) / BK;
