@@ -27,10 +27,8 @@ Three modes:
   ``bf16`` the non-FP8 variant ("Blackwell and Beyond Four GPUs" weighs the
            FP8 cache against one without FP8): the same fp32 rotation, then
            keys and values rounded to bfloat16 (nearest, ties to even); no
-           quantisation scale enters the values. Calibration records one
-           power-of-two factor per head and tensor (2^e with the absmax in
-           [256, 512) * 2^e), which the GPU uses to move bf16 values into
-           fp16 range exactly; attention is in fp64 on the bf16 values.
+           quantisation scale enters the values, so calibration only marks the
+           session as started; attention is in fp64 on the bf16 values.
   ``fp64`` the same ring with exact arithmetic and no quantisation, used to pin
            the ring against the plain linear definition.
 
@@ -78,6 +76,7 @@ class RingCache:
         self.last_pos0 = None    # first position of the most recent write
         self.last_n = 0
         self.scale_k = self.inv_k = self.scale_v = self.inv_v = None
+        self.calibrated = False
 
     # ---- ring bookkeeping (integer, exact) --------------------------------
     @property
@@ -103,15 +102,6 @@ class RingCache:
             return np.float32(1.0), np.float32(1.0)
         return np.float32(float(m) / 448.0), np.float32(448.0 / float(m))
 
-    @staticmethod
-    def _pow2_pair(m: float):
-        """bf16 mode: (2^e, 2^-e) with m * 2^-e in [256, 512); (1, 1) for m = 0."""
-        if m == 0.0:
-            return np.float32(1.0), np.float32(1.0)
-        _, ex = math.frexp(float(m))          # m = f * 2^ex, f in [0.5, 1)
-        e = min(max(ex - 9, -126), 127)
-        return np.float32(math.ldexp(1.0, e)), np.float32(math.ldexp(1.0, -e))
-
     def calibrate(self, k, v):
         """Per-head scales from one frame ``[n, H, d]`` at the next write's positions."""
         k = np.asarray(k, dtype=np.float32)
@@ -120,16 +110,18 @@ class RingCache:
         if self.mode == "fp64":
             raise ValueError("fp64 mode has no quantisation scales")
         self._check_positions(n)
+        self.calibrated = True
+        if self.mode == "bf16":
+            return                      # bf16 storage carries no scale
         c, s = rope.cos_sin(self.next_pos + np.arange(n), self.d, self.base)
         kr = rope.rotate(k, c[:, None, :], s[:, None, :])
         mk = np.abs(kr).max(axis=(0, 2))
         mv = np.abs(v).max(axis=(0, 2))
-        pair = self._pow2_pair if self.mode == "bf16" else self._scale_pair
         sk, ik, sv, iv = [], [], [], []
         for h in range(self.H):
-            a, b = pair(float(mk[h]))
+            a, b = self._scale_pair(float(mk[h]))
             sk.append(a); ik.append(b)
-            a, b = pair(float(mv[h]))
+            a, b = self._scale_pair(float(mv[h]))
             sv.append(a); iv.append(b)
         self.scale_k = np.array(sk, dtype=np.float32)
         self.inv_k = np.array(ik, dtype=np.float32)
@@ -137,7 +129,9 @@ class RingCache:
         self.inv_v = np.array(iv, dtype=np.float32)
 
     def scales(self) -> np.ndarray:
-        """``[4, H]`` fp32: scale_k, inv_k, scale_v, inv_v."""
+        """``[4, H]`` fp32: scale_k, inv_k, scale_v, inv_v (fp8 mode)."""
+        if self.mode != "fp8":
+            raise ValueError("only the fp8 mode has quantisation scales")
         return np.stack([self.scale_k, self.inv_k, self.scale_v, self.inv_v])
 
     # ---- write --------------------------------------------------------------
@@ -171,7 +165,7 @@ class RingCache:
             self.k[:, slots, :] = np.transpose(k8, (1, 0, 2))
             self.v[:, slots, :] = np.transpose(v8, (1, 0, 2))
         elif self.mode == "bf16":
-            if self.inv_k is None:
+            if not self.calibrated:
                 raise RuntimeError("write before calibrate")
             c, s = rope.cos_sin(pos, self.d, self.base)
             kr = rope.rotate(k, c[:, None, :], s[:, None, :])

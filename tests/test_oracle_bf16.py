@@ -1,9 +1,6 @@
 """Pins of the oracle's bfloat16 codec and of the ring's bf16 mode (the non-FP8
 cache variant): torch's bfloat16 conversion, exact round trips, agreement of the
-bf16 ring with the exact ring and with re-rotation from scratch, and the closed
-form of the power-of-two staging factors."""
-import math
-
+bf16 ring with the exact ring and with re-rotation from scratch."""
 import numpy as np
 import pytest
 import torch
@@ -94,14 +91,3 @@ def test_bf16_rebase_equals_rerotation_from_scratch():
     norm = np.repeat(norm, 2, axis=-1)
     assert np.all(np.abs(got - want) <= norm * 3 * 2.0 ** -8 + 1e-30)
     assert np.array_equal(rb.pos[:rb.n_valid], before_pos - delta)
-
-
-def test_pow2_staging_factors_closed_form():
-    rng = np.random.default_rng(3)
-    for m in np.concatenate([rng.uniform(1e-6, 1e6, 200), [1.0, 256.0, 511.999, 512.0, 1e-30]]):
-        sc, inv = RingCache._pow2_pair(float(np.float32(m)))
-        e = round(math.log2(float(sc)))
-        assert float(sc) == 2.0 ** e and float(inv) == 2.0 ** -e
-        y = float(np.float32(m)) / float(sc)
-        assert 256.0 <= y < 512.0 or e in (-126, 127)
-    assert RingCache._pow2_pair(0.0) == (1.0, 1.0)

@@ -101,8 +101,51 @@ def test_saturation_and_signed_zero():
     assert e4m3.encode(x).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x00, 0x80, 0x80]
 
 
-def test_quantize_rounds_scaled_value_once():
-    x = np.array([1.0, 3.0, -7.5], np.float32)
-    inv = np.float32(1.0 / 3.0)
-    y = (x * inv).astype(np.float32)
-    assert np.array_equal(e4m3.quantize(x, inv), e4m3.encode(y))
+# Quantiser pin: the scaled value is rounded to fp32 once before encoding
+# ("Do It Once, at Write Time" stores each element as the E4M3 code of
+# value x inverse scale; the reading fixes that product as one fp32 multiply).
+# Each case is (x, inv, code), x and inv given as fp32 bit patterns. The exact
+# product x * inv lies within a quarter of an fp32 ulp of a midpoint m between
+# two adjacent E4M3 values, so fl32(x * inv) == m and ties-to-even picks the
+# even code; the exact product lies on the other side of m, so a quantiser
+# that encoded it without the fp32 rounding would pick the odd code.
+#   x = m (1 + 2^-12), inv = 1 - 2^-12 + 2^-24: product m (1 + 2^-36), above m
+#   x = m (1 + 2^-13), inv = 1 - 2^-13:         product m (1 - 2^-26), below m
+_INV_ABOVE = 0x3F7FF001      # 1 - 2^-12 + 2^-24
+_INV_BELOW = 0x3F7FF800      # 1 - 2^-13
+QUANTISER_CASES = [
+    # midpoint  x bits       inv bits    code (the even neighbour)
+    (1.0625,    0x3F880880, _INV_ABOVE, 0x38),   # between 0x38 = 1.0 and 0x39 = 1.125
+    (1.1875,    0x3F9804C0, _INV_BELOW, 0x3A),   # between 0x39 = 1.125 and 0x3A = 1.25
+    (0.0029296875, 0x3B400600, _INV_BELOW, 0x02),  # subnormals 0x01 = 2^-9 and 0x02
+    (0.0048828125, 0x3BA00A00, _INV_ABOVE, 0x02),  # subnormals 0x02 and 0x03
+    (0.0146484375, 0x3C700780, _INV_BELOW, 0x08),  # largest subnormal 0x07 and 0x08 = 2^-6
+    (0.033203125, 0x3D080880, _INV_ABOVE, 0x10),   # between 0x10 = 2^-5 and 0x11
+    (21.0,      0x41A80A80, _INV_ABOVE, 0x5A),   # between 0x5A = 20 and 0x5B = 22
+    (432.0,     0x43D806C0, _INV_BELOW, 0x7E),   # between 0x7D = 416 and 0x7E = 448
+]
+
+
+def _f32(bits):
+    return np.array([bits], np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("mid,xb,ib,code", QUANTISER_CASES)
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_quantize_rounds_the_scaled_value_to_fp32_once(mid, xb, ib, code, sign):
+    x, inv = _f32(xb) * np.float32(sign), _f32(ib)
+    assert float((x * inv).astype(np.float32)[0]) == sign * mid     # fl32 lands on the midpoint
+    want = code | (0x80 if sign < 0 else 0)
+    assert int(e4m3.quantize(x, inv)[0]) == want
+
+
+@pytest.mark.parametrize("mid,xb,ib,code", QUANTISER_CASES)
+def test_quantiser_cases_separate_one_rounding_from_none(mid, xb, ib, code):
+    """The exact product's nearest E4M3 value is the other neighbour of the
+    midpoint: a quantiser without the fp32 rounding step fails the case above."""
+    from fractions import Fraction
+    p = Fraction(float(_f32(xb)[0])) * Fraction(float(_f32(ib)[0]))
+    vals = [Fraction(float(v)) for v in e4m3.decode(np.arange(0, 0x7F))]
+    nearest = min(range(len(vals)), key=lambda c: (abs(vals[c] - p), c % 2))
+    assert p != Fraction(mid) and nearest != code
+    assert {nearest, code} == {code, code + (1 if p > Fraction(mid) else -1)}
