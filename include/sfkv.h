@@ -71,13 +71,20 @@ typedef enum { SFKV_BF16 = 0, SFKV_FP32 = 1 } sfkv_dtype;
 
 /* Element storage of the cached keys and values.
  * SFKV_STORE_E4M3: one OCP E4M3 byte per element with per-head fp32 scales
- *   ("Halving the Cache": FP8 with per-head scales).
+ *   ("Do It Once, at Write Time": FP8 quantisation with per-head scales,
+ *   calibrated once per session; "Blackwell and Beyond Four GPUs": the FP8
+ *   cache and its per-head scales).
  * SFKV_STORE_BF16: two bytes per element, the rotated key and the value each
  *   rounded once to bfloat16 (round to nearest even), no quantisation scale
  *   ("Blackwell and Beyond Four GPUs" weighs the FP8 cache against one without
  *   FP8). Its scale slots hold one power-of-two factor per head and tensor,
- *   2^e with the calibration frame's absmax in [256, 512) * 2^e, by which the
- *   attention moves bf16 values into fp16 exactly. */
+ *   2^e with the calibration frame's absmax in [1, 2) * 2^e, by which the
+ *   attention moves bf16 values into fp16 exactly.
+ *   Range contract of this storage: the attention saturates a value v of head
+ *   h at +-65504 * 2^e_v(h), that is at no less than 32,752 times the
+ *   calibration frame's absmax of V for that head (keys have no such bound).
+ *   Values within it are used exactly; a frame carrying larger values should
+ *   be preceded by a new calibration. */
 typedef enum { SFKV_STORE_E4M3 = 0, SFKV_STORE_BF16 = 1 } sfkv_storage;
 
 typedef struct {
@@ -118,7 +125,7 @@ void sfkv_cache_destroy(sfkv_cache *cache);
  * frame of the keys rotated at the positions the next write will use, and of
  * the raw values; scale = absmax/448 and inv = 448/absmax, divided in fp64 and
  * rounded once to fp32 (1 and 1 for an all-zero head). With bf16 storage the
- * pair is instead 2^e and 2^-e with absmax in [256, 512) * 2^e (see
+ * pair is instead 2^e and 2^-e with absmax in [1, 2) * 2^e (see
  * sfkv_storage). Does not advance the ring. May be called again to
  * re-calibrate.
  * Errors: EINVAL (pointers, dtype, n_tokens outside [1, max_new_tokens]),
@@ -189,6 +196,23 @@ sfkv_status sfkv_write_attend(sfkv_cache *cache, const void *k, const void *v, c
  * Source: "Do It Once, at Write Time" (positions reset every 42 steps; a single
  * delta rotation of the cached window at each reset). */
 sfkv_status sfkv_rebase_positions(sfkv_cache *cache, int64_t delta, void *stream);
+
+/* sfkv_rebase_positions_many: the position reset of many caches at once, with
+ * the result of calling sfkv_rebase_positions(caches[i], deltas[i]) for every
+ * i, bit for bit. caches and deltas are host arrays of `count` entries (the
+ * deltas are read during the call only); the caches must be distinct. Caches
+ * that share storage, num_heads, head_dim, capacity and RoPE table are rotated
+ * together, up to 128 per kernel launch, so a reset of every cache of a step is
+ * one or two launches rather than one per cache.
+ * Errors: EINVAL (count < 0, NULL arrays or entries, a cache listed twice),
+ *         ERANGE (some deltas[i] < 0 or > next_pos of caches[i]); on either
+ *         nothing is enqueued and no state changes. EHIP: the caches whose
+ *         launch was enqueued before the failing one are rebased, the others
+ *         are unchanged.
+ * Source: "Do It Once, at Write Time" (every cache gets one delta rotation at
+ * each reset, every 42 steps); "Where the Time Went" (240 caches per step). */
+sfkv_status sfkv_rebase_positions_many(sfkv_cache *const *caches, const int64_t *deltas,
+                                       int32_t count, void *stream);
 
 /* Host mirror of the ring state (no device access). Any out pointer may be NULL.
  * tokens: written this session; next_pos: position of the next token;

@@ -212,11 +212,14 @@ __global__ __launch_bounds__(kCalibrateThreads) void calibrate_kernel(CalibrateL
     m = fmaxf(m, partial[0]);
     float scale = 1.0f, inv = 1.0f;
     if (m > 0.0f && a.storage == kBF16) {
-      // power of two 2^e with m * 2^-e in [256, 512): moves bf16 values into
-      // fp16 range exactly when the attention stages them
+      // power of two 2^e with m * 2^-e in [1, 2): moves bf16 values into fp16
+      // range exactly when the attention stages them, with 65504 / 2 = 32752
+      // times the calibration frame's absmax of headroom above it (the
+      // attention saturates values beyond 65504 * 2^e; smaller values keep
+      // fp16's 11 bits down to 2^-14 * 2^e)
       int ex;
       frexp(static_cast<double>(m), &ex);   // m = f * 2^ex, f in [0.5, 1)
-      int e = ex - 9;
+      int e = ex - 1;
       e = e < -126 ? -126 : (e > 127 ? 127 : e);
       scale = ldexpf(1.0f, e);
       inv = ldexpf(1.0f, -e);
@@ -230,65 +233,89 @@ __global__ __launch_bounds__(kCalibrateThreads) void calibrate_kernel(CalibrateL
   }
 }
 
-// Delta rotation of the cached keys, one head per grid row. A thread owns one
-// 16-byte column chunk (8 code pairs) and two rows of its wave's slab, so its 8
-// cos/sin pairs are loaded once per two rows and both 16-byte loads are in
-// flight before the first store. The lanes of a wave cover 64 / (D/16)
-// consecutive rows completely at each step, so every load and store is one
-// contiguous kilobyte per wave. Each code pair is decoded exactly to fp32,
-// rotated by -delta, clamped and re-encoded in place; the per-head scale
-// cancels because the rotation is linear.
+// Delta rotation of one 16-byte chunk of a cached key row (E4M3: 8 code
+// pairs; bf16: 4 pairs): each pair decoded exactly to fp32, rotated by -delta
+// with the table row of delta (t: the chunk's pairs), then clamped and
+// re-encoded (E4M3) or rounded to bf16. The per-head scale cancels because
+// the rotation is linear.
+template <int ST>
+__device__ inline uint4 rebase_chunk(uint4 w, const RopePair *t) {
+  if constexpr (ST == kBF16) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float x0 = __uint_as_float(u[k] << 16), x1 = __uint_as_float(u[k] & 0xffff0000u);   // exact
+      rotate_pair_back(x0, x1, t[k]);
+      o[k] = pack_bf16(x0, x1);
+    }
+    return uint4{o[0], o[1], o[2], o[3]};
+  } else {
+    float x[16];
+    decode4(w.x, x);
+    decode4(w.y, x + 4);
+    decode4(w.z, x + 8);
+    decode4(w.w, x + 12);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rotate_pair_back(x[2 * k], x[2 * k + 1], t[k]);
+    uint4 o;
+    o.x = encode4(x[0], x[1], x[2], x[3]);
+    o.y = encode4(x[4], x[5], x[6], x[7]);
+    o.z = encode4(x[8], x[9], x[10], x[11]);
+    o.w = encode4(x[12], x[13], x[14], x[15]);
+    return o;
+  }
+}
+
+// Delta rotation of the cached keys of up to kRebaseBatch caches in one
+// launch (a position reset of every cache of a step is one launch, not one per
+// cache). Work unit = (cache, head, block of rows); workgroups
+// stride over the units. In a unit each thread owns one 16-byte column chunk
+// of J rows of its wave's slab, loads all J before the first store, and
+// loads its chunk's cos/sin pairs once; the lanes of a wave cover 64 / (chunks
+// per row) consecutive rows completely at each step, so every load and store
+// is one contiguous kilobyte per wave. Rows at or past a cache's n_valid are
+// left alone. For head 0, chunk 0 also moves the slot's position by -delta.
 template <int D, int ST>
 __global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunch a) {
   constexpr int ES = ST == kBF16 ? 2 : 1;       // bytes per element
   constexpr int CH = D * ES / 16;       // 16-byte chunks per row
   constexpr int PAIRS = 8 / ES;         // code pairs per 16-byte chunk
   constexpr int RSTEP = 64 / CH;        // rows one wave covers per step
-  constexpr int J = 2;                  // steps per thread
-  const int h = blockIdx.y;
+  constexpr int J = kRebaseRowsPerThread;
+  constexpr int ROWS = 4 * RSTEP * J;   // rows per unit
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane % CH;
-  const int slot0 = (blockIdx.x * 4 + wave) * (RSTEP * J) + lane / CH;
-  uint8_t *base = a.k8 + static_cast<size_t>(h) * a.capacity * D * ES + c * 16;
-  const RopePair *cs = a.rope_row + c * PAIRS;
-  RopePair t[PAIRS];
+  const int rblocks = (a.max_valid + ROWS - 1) / ROWS;
+  const int per_cache = a.heads * rblocks;
+  const int units = a.count * per_cache;
+  const size_t plane_row = static_cast<size_t>(D) * ES;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int e = u / per_cache;
+    const int rem = u - e * per_cache;
+    const int h = rem / rblocks;
+    const int rb = rem - h * rblocks;
+    const RebaseEntry en = a.entry[e];
+    const int slot0 = rb * ROWS + wave * (RSTEP * J) + lane / CH;
+    uint8_t *base = en.base + static_cast<size_t>(h) * a.capacity * plane_row + c * 16;
+    const RopePair *cs = a.rope + static_cast<size_t>(en.delta) * (D / 2) + c * PAIRS;
+    RopePair t[PAIRS];
 #pragma unroll
-  for (int k = 0; k < PAIRS; ++k) t[k] = cs[k];
-  uint4 w[J];
+    for (int k = 0; k < PAIRS; ++k) t[k] = cs[k];
+    uint4 w[J];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int slot = slot0 + j * RSTEP;
-    if (slot < a.n_valid) w[j] = *reinterpret_cast<const uint4 *>(base + static_cast<size_t>(slot) * D * ES);
-  }
+    for (int j = 0; j < J; ++j) {
+      const int slot = slot0 + j * RSTEP;
+      if (slot < en.n_valid) w[j] = *reinterpret_cast<const uint4 *>(base + static_cast<size_t>(slot) * plane_row);
+    }
+    int32_t *pos = reinterpret_cast<int32_t *>(en.base + a.pos_off);
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int slot = slot0 + j * RSTEP;
-    if (slot < a.n_valid && ST == kBF16) {
-      const uint32_t u[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float x0 = __uint_as_float(u[k] << 16), x1 = __uint_as_float(u[k] & 0xffff0000u);   // exact
-        rotate_pair_back(x0, x1, t[k]);
-        o[k] = pack_bf16(x0, x1);
+    for (int j = 0; j < J; ++j) {
+      const int slot = slot0 + j * RSTEP;
+      if (slot < en.n_valid) {
+        *reinterpret_cast<uint4 *>(base + static_cast<size_t>(slot) * plane_row) = rebase_chunk<ST>(w[j], t);
+        if (h == 0 && c == 0) pos[slot] -= en.delta;
       }
-      *reinterpret_cast<uint4 *>(base + static_cast<size_t>(slot) * D * ES) = uint4{o[0], o[1], o[2], o[3]};
-      if (h == 0 && c == 0) a.pos[slot] -= a.delta;
-    } else if (slot < a.n_valid) {
-      float x[16];
-      decode4(w[j].x, x);
-      decode4(w[j].y, x + 4);
-      decode4(w[j].z, x + 8);
-      decode4(w[j].w, x + 12);
-#pragma unroll
-      for (int k = 0; k < PAIRS; ++k) rotate_pair_back(x[2 * k], x[2 * k + 1], t[k]);
-      uint4 o;
-      o.x = encode4(x[0], x[1], x[2], x[3]);
-      o.y = encode4(x[4], x[5], x[6], x[7]);
-      o.z = encode4(x[8], x[9], x[10], x[11]);
-      o.w = encode4(x[12], x[13], x[14], x[15]);
-      *reinterpret_cast<uint4 *>(base + static_cast<size_t>(slot) * D) = o;
-      if (h == 0 && c == 0) a.pos[slot] -= a.delta;
     }
   }
 }
@@ -360,13 +387,14 @@ hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s) {
-  if (a.n_valid <= 0 || a.heads <= 0) return hipSuccess;
-  // rows per workgroup: 4 waves x (64 / (16-byte chunks per row)) rows x 2 steps
+hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s, int cus) {
+  if (a.count <= 0 || a.max_valid <= 0 || a.heads <= 0) return hipSuccess;
   const int es = a.storage == kBF16 ? 2 : 1;
-  const int rows_per_block = 4 * (64 / (a.head_dim * es / 16)) * 2;
-  const dim3 grid(static_cast<unsigned>((a.n_valid + rows_per_block - 1) / rows_per_block),
-                  static_cast<unsigned>(a.heads));
+  const int rows = 4 * (64 / (a.head_dim * es / 16)) * kRebaseRowsPerThread;
+  const int64_t units = static_cast<int64_t>(a.count) * a.heads * ((a.max_valid + rows - 1) / rows);
+  // eight resident workgroups per CU stride over the units
+  const int64_t cap = 8 * static_cast<int64_t>(cus > 0 ? cus : 256);
+  const dim3 grid(static_cast<unsigned>(units < cap ? units : cap));
   if (a.storage == kBF16) {
     if (a.head_dim == 128) hipLaunchKernelGGL((rebase_kernel<128, kBF16>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((rebase_kernel<64, kBF16>), grid, dim3(256), 0, s, a);

@@ -9,6 +9,7 @@
 #include "sfkv.h"
 #include "sfkv_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -391,29 +392,80 @@ sfkv_status sfkv_write_attend(sfkv_cache *c, const void *k, const void *v, const
   return launched(sfkv::launch_attend(a, as_stream(stream)));
 }
 
+// Caches that can share one rebase launch: same storage, shape and RoPE table.
+static bool same_rebase_group(const sfkv_cache *a, const sfkv_cache *b) {
+  return a->cfg.storage == b->cfg.storage && a->cfg.num_heads == b->cfg.num_heads &&
+         a->cfg.head_dim == b->cfg.head_dim && a->cfg.capacity == b->cfg.capacity && a->rope == b->rope;
+}
+
+static void rebased(sfkv_cache *c, int64_t delta) {
+  c->next_pos -= delta;
+  c->last_pos0 -= delta;
+}
+
+// Launches the delta rotations of caches[0 .. count-1] (validated, distinct),
+// grouped by configuration, at most kRebaseBatch per launch; moves each
+// cache's host state once its launch has been enqueued.
+static sfkv_status rebase_caches(sfkv_cache *const *caches, const int64_t *deltas, int32_t count,
+                                 void *stream) {
+  std::vector<char> done(static_cast<size_t>(count), 0);
+  for (int32_t i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    if (deltas[i] == 0 || n_valid_of(caches[i]) == 0) {   // nothing on the device to move
+      rebased(caches[i], deltas[i]);
+      done[i] = 1;
+      continue;
+    }
+    const sfkv_cache *lead = caches[i];
+    sfkv::RebaseLaunch a;
+    a.rope = lead->rope->table;
+    a.pos_off = lead->pos_off;
+    a.storage = storage_of(lead->cfg);
+    a.heads = lead->cfg.num_heads;
+    a.head_dim = lead->cfg.head_dim;
+    a.capacity = lead->cfg.capacity;
+    a.count = 0;
+    a.max_valid = 0;
+    int32_t members[sfkv::kRebaseBatch];
+    for (int32_t j = i; j < count && a.count < sfkv::kRebaseBatch; ++j) {
+      if (done[j] || deltas[j] == 0 || n_valid_of(caches[j]) == 0 || !same_rebase_group(lead, caches[j]))
+        continue;
+      const int nv = n_valid_of(caches[j]);
+      a.entry[a.count] = sfkv::RebaseEntry{caches[j]->base, nv, static_cast<int32_t>(deltas[j])};
+      members[a.count++] = j;
+      if (nv > a.max_valid) a.max_valid = nv;
+    }
+    const sfkv_status st = launched(sfkv::launch_rebase(a, as_stream(stream), lead->cus));
+    if (st != SFKV_OK) return st;
+    for (int32_t m = 0; m < a.count; ++m) {
+      rebased(caches[members[m]], deltas[members[m]]);
+      done[members[m]] = 1;
+    }
+  }
+  return ok();
+}
+
 sfkv_status sfkv_rebase_positions(sfkv_cache *c, int64_t delta, void *stream) {
   if (!c) return fail(SFKV_EINVAL, "cache is NULL");
   if (delta < 0 || delta > c->next_pos) return fail(SFKV_ERANGE, "delta must be in [0, next_pos]");
-  if (delta > 0) {
-    const int nv = n_valid_of(c);
-    if (nv > 0) {
-      sfkv::RebaseLaunch a;
-      a.storage = storage_of(c->cfg);
-      a.k8 = c->base + c->k_off;
-      a.pos = reinterpret_cast<int32_t *>(c->base + c->pos_off);
-      a.heads = c->cfg.num_heads;
-      a.head_dim = c->cfg.head_dim;
-      a.capacity = c->cfg.capacity;
-      a.n_valid = nv;
-      a.delta = static_cast<int>(delta);
-      a.rope_row = c->rope->table + static_cast<size_t>(delta) * (c->cfg.head_dim / 2);
-      sfkv_status st = launched(sfkv::launch_rebase(a, as_stream(stream)));
-      if (st != SFKV_OK) return st;
-    }
+  return rebase_caches(&c, &delta, 1, stream);
+}
+
+sfkv_status sfkv_rebase_positions_many(sfkv_cache *const *caches, const int64_t *deltas, int32_t count,
+                                       void *stream) {
+  if (count < 0) return fail(SFKV_EINVAL, "count must be >= 0");
+  if (count == 0) return ok();
+  if (!caches || !deltas) return fail(SFKV_EINVAL, "caches and deltas must be host arrays of count entries");
+  for (int32_t i = 0; i < count; ++i) {
+    if (!caches[i]) return fail(SFKV_EINVAL, "caches[" + std::to_string(i) + "] is NULL");
+    if (deltas[i] < 0 || deltas[i] > caches[i]->next_pos)
+      return fail(SFKV_ERANGE, "deltas[" + std::to_string(i) + "] must be in [0, next_pos] of its cache");
   }
-  c->next_pos -= delta;
-  c->last_pos0 -= delta;
-  return ok();
+  std::vector<const sfkv_cache *> sorted(caches, caches + count);
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+    return fail(SFKV_EINVAL, "a cache appears more than once");
+  return rebase_caches(caches, deltas, count, stream);
 }
 
 sfkv_status sfkv_cache_state(const sfkv_cache *c, int64_t *tokens, int64_t *next_pos,

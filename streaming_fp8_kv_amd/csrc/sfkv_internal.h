@@ -36,13 +36,25 @@ struct CalibrateLaunch {
   float *scales;
 };
 
+// Delta rotation of the keys of up to kRebaseBatch caches of one
+// configuration (storage, heads, head_dim, capacity) and one RoPE table in one
+// launch. Each cache's buffer starts with its K plane (offset 0 of the cache
+// layout); its positions sit at pos_off. The whole argument block travels as
+// kernel arguments (2 KB), so a captured launch carries its own copy.
+constexpr int kRebaseBatch = 128;
+constexpr int kRebaseRowsPerThread = 4;
+struct RebaseEntry {
+  uint8_t *base;     // the cache's device buffer
+  int32_t n_valid;   // valid slots (rows 0 .. n_valid - 1 of every head)
+  int32_t delta;     // rotation by -delta; positions drop by delta
+};
 struct RebaseLaunch {
-  int storage;
-  uint8_t *k8;
-  int32_t *pos;
-  int heads, head_dim, capacity, n_valid;
-  int delta;
-  const RopePair *rope_row;  // table row at position delta
+  const RopePair *rope;      // the table, [max_position + 1][head_dim / 2]
+  size_t pos_off;            // byte offset of positions[] in a cache's buffer
+  int storage, heads, head_dim, capacity;
+  int count;                 // entries used
+  int max_valid;             // largest n_valid among them
+  RebaseEntry entry[kRebaseBatch];
 };
 
 struct AttendLaunch {
@@ -77,7 +89,7 @@ struct ShiftLaunch {
 hipError_t launch_shift(const ShiftLaunch &a, hipStream_t s);
 hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s);
 hipError_t launch_write(const WriteLaunch &a, hipStream_t s);
-hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s);
+hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s, int cus);
 hipError_t launch_attend(const AttendLaunch &a, hipStream_t s);
 // One launch: the write `w` and the query preparation of `q` (the same frame's
 // queries), with q.queries_ready ignored.

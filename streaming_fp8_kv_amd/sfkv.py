@@ -8,7 +8,8 @@ is no fallback implementation.
 The function names mirror the C entry points without their ``sfkv_`` prefix:
 ``rope_bytes``, ``rope_init``, ``cache_bytes``, ``cache_init``,
 ``calibrate_scales``, ``cache_write``, ``attend_workspace_bytes``, ``attend``,
-``rebase_positions``, ``cache_state``, ``cache_layout``, and for the launch
+``write_attend``, ``rebase_positions``, ``rebase_positions_many``,
+``cache_state``, ``cache_layout``, and for the launch
 software's plain linear window ``linear_bytes``, ``linear_init``,
 ``linear_calibrate_scales``, ``linear_write``, ``linear_workspace_bytes``,
 ``linear_attend``, ``linear_state``, ``linear_layout``. ``Rope``,
@@ -39,6 +40,7 @@ SYMBOLS = (
     "sfkv_cache_bytes", "sfkv_cache_init", "sfkv_cache_destroy",
     "sfkv_calibrate_scales", "sfkv_cache_write",
     "sfkv_attend_workspace_bytes", "sfkv_attend", "sfkv_write_attend", "sfkv_rebase_positions",
+    "sfkv_rebase_positions_many",
     "sfkv_cache_state", "sfkv_cache_layout",
     "sfkv_linear_bytes", "sfkv_linear_init", "sfkv_linear_destroy",
     "sfkv_linear_calibrate_scales", "sfkv_linear_write", "sfkv_linear_workspace_bytes",
@@ -79,6 +81,7 @@ _sig("sfkv_attend_workspace_bytes", _sz, _vp)
 _sig("sfkv_attend", ctypes.c_int, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
 _sig("sfkv_write_attend", ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
 _sig("sfkv_rebase_positions", ctypes.c_int, _vp, _i64, _vp)
+_sig("sfkv_rebase_positions_many", ctypes.c_int, _P(_vp), _P(_i64), _i32, _vp)
 _sig("sfkv_cache_state", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i32), _P(_i32))
 _sig("sfkv_cache_layout", ctypes.c_int, _vp, _P(_sz), _P(_sz), _P(_sz), _P(_sz))
 _sig("sfkv_linear_bytes", _sz, _P(CacheConfig), ctypes.c_int)
@@ -185,6 +188,16 @@ def write_attend(handle: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
 
 def rebase_positions(handle: int, delta: int, stream=None):
     _check(_lib.sfkv_rebase_positions(handle, int(delta), _stream(stream)))
+
+
+def rebase_positions_many(handles, deltas, stream=None):
+    """One delta rotation per cache: handles[i] by deltas[i], as few launches."""
+    handles, deltas = list(handles), [int(d) for d in deltas]
+    if len(handles) != len(deltas):
+        raise ValueError("one delta per cache")
+    hs = (_vp * len(handles))(*handles)
+    ds = (_i64 * len(deltas))(*deltas)
+    _check(_lib.sfkv_rebase_positions_many(hs, ds, len(handles), _stream(stream)))
 
 
 def cache_state(handle: int) -> dict:

@@ -1,10 +1,12 @@
 """The per-step sweep: many independent ring caches, each written and attended
 once per diffusion step, in order, on one stream.
 
-One step of the production model is 60 blocks x 4 denoising passes = 240
-attention calls, and each call reads its own cache of 5,788 slots with 757 new
-tokens (Runway Characters post, "Where the Time Went"). Calls are issued one
-after another because in the model each block depends on the previous one.
+Shape of one step, as the Runway Characters post gives it ("Where the Time
+Went"): the model has 60 blocks and runs 4 denoising passes per step, so a
+step makes 240 attention calls; every call has a private ring (5,788 slots),
+into which each step adds one frame of 757 tokens. The calls go out one by
+one on a single stream, since each block consumes the previous block's
+output.
 
 Inputs are drawn on the device from per-cache seeded generators (seed
 ``spec.seed * 1000 + cache index``) with the production-call distribution.
@@ -78,6 +80,7 @@ class Sweep:
                 self.sfkv.attend(c.handle, q, out, self.workspace, stream)
 
     def reset_all(self, stream=None):
-        """Position reset of every cache: one delta rotation each (to position 0)."""
-        for c in self.caches:
-            c.rebase_positions(c.state()["next_pos"], stream)
+        """Position reset of every cache (each back to position 0): one delta
+        rotation per cache, all issued through one batched call."""
+        self.sfkv.rebase_positions_many([c.handle for c in self.caches],
+                                        [c.state()["next_pos"] for c in self.caches], stream)

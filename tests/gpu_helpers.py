@@ -15,7 +15,7 @@ import sys
 import numpy as np
 import torch
 
-from oracle import bf16, e4m3
+from oracle import bf16, e4m3, rope as orope
 from oracle.cache import RingCache as OracleCache, softmax_attention
 
 A_MAX = 2e-2
@@ -61,6 +61,9 @@ class Mirror:
 
     def calibrate(self, k, v):
         self.gpu.calibrate_scales(k.cuda(), v.cuda())
+        if self.bf16:
+            self.factors = bf16_staging_factors(self._sub(k), self._sub(v), self.ora.next_pos,
+                                                self.spec.shape.rope_base)
         self.ora.calibrate(self._sub(k), self._sub(v))
 
     def write(self, k, v):
@@ -86,7 +89,8 @@ class Mirror:
         pos = self.gpu.positions().cpu().numpy()
         assert np.array_equal(pos[:nv], self.ora.pos[:nv]), f"{tag}: positions differ"
         sc = self.gpu.scales()[:, hs].cpu().numpy()
-        assert np.array_equal(sc, self.ora.scales()), f"{tag}: scales differ"
+        want = self.factors if self.bf16 else self.ora.scales()
+        assert np.array_equal(sc, want), f"{tag}: scales differ"
 
     def reference_from_gpu_cache(self, q, rows):
         """Oracle attention over the GPU's own codes and scales (checked heads)."""
@@ -118,6 +122,36 @@ class Mirror:
         say(f"  {tag}: attention A={a:.2e} B={b:.2e} over {len(rows)} rows x {len(self.heads)} heads")
         assert a <= A_MAX and b <= B_MEAN, f"{tag}: A={a:.3e} (bar {A_MAX}) B={b:.3e} (bar {B_MEAN})"
         return out
+
+
+def bf16_staging_factors(k, v, pos0, base):
+    """Expected scale slots of a bf16-storage cache after calibration on frame
+    (k, v) ``[n, H, d]`` at positions pos0..: per head and tensor the power of two
+    2^e with the frame's absmax in [1, 2) * 2^e (keys rotated as written), as
+    ``[4, H]`` (2^e_k, 2^-e_k, 2^e_v, 2^-e_v); 1 and 1 for an all-zero head.
+
+    These are the library's own contract for the non-FP8 storage (the factor by
+    which its attention moves bf16 values into fp16 range), not part of the
+    method, so they are written out here rather than in the oracle."""
+    k = np.asarray(k, np.float32)
+    v = np.asarray(v, np.float32)
+    n, H, d = k.shape
+    c, s_ = orope.cos_sin(pos0 + np.arange(n), d, base)
+    kr = orope.rotate(k, c[:, None, :], s_[:, None, :])
+    out = np.ones((4, H), np.float32)
+    for row, x in ((0, kr), (2, v)):
+        m = np.abs(x).max(axis=(0, 2)).astype(np.float64)
+        for h in range(H):
+            if m[h] > 0:
+                e = int(np.floor(np.log2(m[h])))
+                if 2.0 ** e > m[h]:
+                    e -= 1
+                elif 2.0 ** (e + 1) <= m[h]:
+                    e += 1
+                e = min(max(e, -126), 127)
+                out[row, h] = np.float32(2.0 ** e)
+                out[row + 1, h] = np.float32(2.0 ** -e)
+    return out
 
 
 def spread_rows(n, k):

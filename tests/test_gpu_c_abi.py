@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from streaming_fp8_kv_amd import workloads as W
-from tests.gpu_helpers import A_MAX, B_MEAN, attention_error, say
+from tests.gpu_helpers import A_MAX, B_MEAN, attention_error, bf16_staging_factors, say
 
 pytestmark = pytest.mark.gpu
 
@@ -82,4 +82,8 @@ def test_c_session_matches_oracle(tmp_path, storage):
     assert np.array_equal(k_plane[:, :nv], ora.k[:, :nv])
     assert np.array_equal(v_plane[:, :nv], ora.v[:, :nv])
     assert np.array_equal(pos[:nv], ora.pos[:nv])
-    assert np.array_equal(scales, ora.scales())
+    if storage == "bf16":
+        want = bf16_staging_factors(data[0][1].float().numpy(), data[0][2].float().numpy(), 0, s.rope_base)
+    else:
+        want = ora.scales()
+    assert np.array_equal(scales, want)

@@ -113,6 +113,12 @@ def test_null_handles(sfkv):
     assert lib.sfkv_attend(None, 256, 0, 1, 256, None, 0, None) == sfkv.EINVAL
     assert lib.sfkv_write_attend(None, 256, 256, 256, 0, 1, 256, None, 0, None) == sfkv.EINVAL
     assert lib.sfkv_rebase_positions(None, 0, None) == sfkv.EINVAL
+    assert lib.sfkv_rebase_positions_many(None, None, 0, None) == sfkv.OK
+    assert lib.sfkv_rebase_positions_many(None, None, 1, None) == sfkv.EINVAL
+    assert lib.sfkv_rebase_positions_many(None, None, -1, None) == sfkv.EINVAL
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    zeros = (ctypes.c_int64 * 2)(0, 0)
+    assert lib.sfkv_rebase_positions_many(nulls, zeros, 2, None) == sfkv.EINVAL
     assert lib.sfkv_cache_state(None, None, None, None, None) == sfkv.EINVAL
     assert lib.sfkv_attend_workspace_bytes(None) == 0
     assert lib.sfkv_linear_write(None, 256, 256, 1, None) == sfkv.EINVAL
