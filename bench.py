@@ -21,7 +21,8 @@ against the dense FP8 MFMA peak; events around each single call
 (``attend_us_with_events``) add their own few microseconds. One separate attend call is three kernel launches (query prep,
 attention, split combine); the rocprofv3 summary lists each. cache_write
 alone, the fused step captured once as a HIP graph and replayed, and the
-position reset (one delta rotation per cache) are timed in separate regions
+position reset (one delta rotation per cache, through the batched call) are
+timed in separate regions
 after the timed one and reported under ``extra``. So is the same sweep over
 rings that store bf16 instead of E4M3 (``bf16_*``, the non-FP8 variant
 "Blackwell and Beyond Four GPUs" weighs), and the launch software's plain path
@@ -42,14 +43,42 @@ import time
 PEAK_FP8_TFLOPS = 5000.0      # dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
 
-# HBM traffic of one attend call (query prep + attention + merge), from two
-# rocprofv3 --pmc passes over this benchmark: FETCH_SIZE scaled by 1.9972 (a
-# plain scale kernel reading 17.78 MB counts 8,694.0 KiB of FETCH_SIZE; see
-# --copy-calibration) and WRITE_SIZE as counted (its 17.78 MB write counts
-# 17,363.3 KiB): fetch 5.47 + 44.25 + 17.11 MB, write 7.27 + 17.07 + 9.30 MB.
-# Set to None whenever the attend kernels change until the counters are taken
-# again.
-ATTEND_TRAFFIC_BYTES = 100.47e6
+# HBM traffic of one attend call (query prep + attention + merge) comes from
+# two rocprofv3 --pmc passes over this benchmark (FETCH_SIZE scaled by the
+# copy-kernel factor, WRITE_SIZE as counted; see --copy-calibration). The
+# committed summary carries a machine-readable record with the SHA-256 of the
+# sources the counters were taken on; the figure is reported only while those
+# sources are unchanged, and as null otherwise.
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "sfkv_traffic_step24_h24_d128_n757_c5788.md")
+ATTEND_SOURCES = ("streaming_fp8_kv_amd/csrc/attend_kernel.hip", "streaming_fp8_kv_amd/csrc/query_prep.h",
+                  "streaming_fp8_kv_amd/csrc/sfkv_internal.h", "streaming_fp8_kv_amd/csrc/sfkv_api.cpp")
+
+
+def attend_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in ATTEND_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_attend_traffic():
+    """(bytes per attend call, record) from the committed counter summary, or
+    (None, reason) when it is missing or was taken on other sources."""
+    try:
+        lines = open(TRAFFIC_PROFILE).read().splitlines()
+    except OSError:
+        return None, "no traffic profile"
+    recs = [json.loads(ln.split("bench-record:", 1)[1]) for ln in lines if ln.startswith("bench-record:")]
+    if not recs:
+        return None, "no bench-record line in the traffic profile"
+    rec = recs[-1]
+    if rec.get("sources_sha256") != attend_sources_sha256():
+        return None, "attend sources changed since the counters were taken"
+    return float(rec["attend_call_bytes"]), rec
 
 
 def parse():
@@ -59,7 +88,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--calls", type=int, default=240, help="caches (calls) per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-calls", type=int, default=32)
+    ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of each timed oracle step")
     ap.add_argument("--bf16-steps", type=int, default=5,
                     help="timed steps of the same sweep over bf16 rings (0 skips)")
     ap.add_argument("--plain-calls", type=int, default=24,
@@ -90,39 +119,75 @@ def copy_calibration():
         del a, b
 
 
-def cpu_baseline(n_calls: int):
-    """The oracle as it stands, on the host: cache_write + attend of the
-    production call (757 tokens into a wrapped 5,788-slot ring, 24 heads)."""
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(reps: int = 3):
+    """The oracle as it stands, on the host, at the production call (757 new
+    tokens into a wrapped 5,788-slot ring, 24 heads x 128): cache_write, attend
+    (fp64, all 757 rows) and rebase (a reset of the whole ring) each timed
+    `reps` times; medians. A 240-call step and the reset step are extrapolated
+    from them (240 x the per-call medians) and labelled so."""
     import numpy as np
     from oracle.cache import RingCache
+    from oracle import rope
     from streaming_fp8_kv_amd import workloads as W
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    host_cpus = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     spec = W.PROD
     s = spec.shape
     fs = W.FrameStream(spec)
-    frames = [tuple(t.float().numpy() for t in fs.frame()) for _ in range(8 + n_calls)]
+    frames = [tuple(t.float().numpy() for t in fs.frame()) for _ in range(8 + reps)]
     rc = RingCache(s.heads, s.head_dim, s.capacity, s.new_tokens, s.rope_base, s.max_position)
     rc.calibrate(frames[0][1], frames[0][2])
     for _, k, v in frames[:8]:
         rc.write(k, v)                      # prefill (untimed)
     # RoPE rows of the timed positions are computed once, untimed, as the GPU
     # path's table is built at set-up
-    from oracle import rope
-    rope.cos_sin(np.arange(rc.next_pos, rc.next_pos + n_calls * s.new_tokens), s.head_dim, s.rope_base)
-    t0 = time.perf_counter()
+    rope.cos_sin(np.arange(rc.next_pos, rc.next_pos + reps * s.new_tokens), s.head_dim, s.rope_base)
+    rope.cos_sin(np.arange(0, s.new_tokens), s.head_dim, s.rope_base)
+    t_write, t_attend, t_rebase = [], [], []
+    t_begin = time.perf_counter()
     for q, k, v in frames[8:]:
+        t0 = time.perf_counter()
         rc.write(k, v)
+        t1 = time.perf_counter()
         rc.attend(q)
-    dt = time.perf_counter() - t0
-    return {"value": dt / n_calls * 1e6, "unit": "us per cache_write+attend call",
+        t2 = time.perf_counter()
+        t_write.append(t1 - t0)
+        t_attend.append(t2 - t1)
+    for _ in range(reps):
+        rope.cos_sin([rc.next_pos], s.head_dim, s.rope_base)
+        t0 = time.perf_counter()
+        rc.rebase(rc.next_pos)
+        t_rebase.append(time.perf_counter() - t0)
+        rc.write(frames[8][1], frames[8][2])      # untimed: so the next reset has a nonzero delta
+    total = time.perf_counter() - t_begin
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    w_us, a_us, r_us = med(t_write) * 1e6, med(t_attend) * 1e6, med(t_rebase) * 1e6
+    return {"value": round(w_us + a_us, 1), "unit": "us per cache_write+attend call",
             "cores": threads, "kind": "oracle",
-            "sample": f"{n_calls} production calls (757 new tokens, 5,788-slot wrapped ring, "
-                      f"24 heads x 128, fp64 attention over all rows) after an untimed 8-frame prefill; "
-                      f"{dt:.1f} s of CPU time"}
+            "sample": f"production call (757 new tokens, wrapped 5,788-slot ring, 24 heads x 128), "
+                      f"each step timed {reps} times after an untimed 8-frame prefill, medians; "
+                      f"{total:.1f} s of CPU time",
+            "write_us": round(w_us, 1), "attend_us": round(a_us, 1), "rebase_us": round(r_us, 1),
+            "step_ms_extrapolated": round((w_us + a_us) * W.CALLS_PER_STEP / 1e3, 1),
+            "reset_step_extra_ms_extrapolated": round(r_us * W.CALLS_PER_STEP / 1e3, 1),
+            "threads_note": "cores = BLAS threads of the oracle's fp64 matrix products (the rest of "
+                            "the oracle runs on one thread)",
+            "host_cpus": host_cpus, "cpu_model": _cpu_model()}
 
 
 def plain_path(sfkv, W, spec, n_caches: int, stream):
@@ -308,16 +373,30 @@ def main():
     graph_ms = g0.elapsed_time(g1) / args.steps
     del graph
 
-    # ---- position reset: one delta rotation of every cache, back to back
-    # between two events ----
+    # ---- position reset: one delta rotation of every cache's keys. First a
+    # partial rebase (half the positions) as one sfkv_rebase_positions call per
+    # cache, back to back between two events; then the reset to position 0 of
+    # all caches through the batched call (one or two launches), between two
+    # events. Both move every key plane once; the delta does not change the
+    # work. ----
     r0, r1 = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
     r0.record(stream)
     for c in sw.caches:
-        c.rebase_positions(c.state()["next_pos"], stream)
+        c.rebase_positions(c.state()["next_pos"] // 2, stream)
     r1.record(stream)
     torch.cuda.synchronize()
-    rebase_us = r0.elapsed_time(r1) * 1e3 / n_calls
+    rebase_single_us = r0.elapsed_time(r1) * 1e3 / n_calls
+    handles = [c.handle for c in sw.caches]
+    deltas = [c.state()["next_pos"] for c in sw.caches]
+    b0, b1 = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    b0.record(stream)
+    sfkv.rebase_positions_many(handles, deltas, stream)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    reset_ms = b0.elapsed_time(b1)
+    rebase_us = reset_ms * 1e3 / n_calls
 
     plain = plain_path(sfkv, W, spec, args.plain_calls, stream) if args.plain_calls > 0 else None
     if args.bf16_steps > 0:
@@ -333,6 +412,7 @@ def main():
     write_bytes = 2 * n * H * d * 2 + 2 * n * H * d * 1
     rebase_bytes = 2 * H * C * d
     achieved = attend_flops / (attend_us * 1e-6) / 1e12
+    traffic, traffic_rec = profiled_attend_traffic()
     line = {
         "metric": "us per cache_write+attend call at 757x5788 (240-call step)",
         "value": round(ms_per_step * 1e3 / n_calls, 3),
@@ -351,9 +431,11 @@ def main():
                    "input_dtype": "bf16", "cache_dtype": "e4m3"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": ATTEND_TRAFFIC_BYTES,
-                     "kernel": "sfkv_attend (query prep + attention + split combine)",
-                     "launch_us": round(attend_us, 3)},
+                     "traffic": traffic,
+                     "kernel": "sfkv_attend call: query prep + attention + split merge launches",
+                     "launch_us": round(attend_us, 3),
+                     "traffic_source": (f"rocprofv3 FETCH_SIZE x {traffic_rec['fetch_factor']} + WRITE_SIZE, "
+                                        f"{traffic_rec['taken']}" if traffic is not None else traffic_rec)},
         "extra": {
             "attend_us": round(attend_us, 3),
             "attend_us_with_events": round(attend_us_events, 3),
@@ -362,7 +444,9 @@ def main():
             "write_hbm_frac": round(write_bytes / (write_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "rebase_us_per_cache": round(rebase_us, 3),
             "rebase_hbm_frac": round(rebase_bytes / (rebase_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "reset_step_extra_ms": round(rebase_us * n_calls / 1e3, 4),
+            "reset_step_extra_ms": round(reset_ms, 4),
+            "reset_step_launches": -(-n_calls // 128),
+            "rebase_single_call_us_per_cache": round(rebase_single_us, 3),
             "unfused_ms_per_step": round(unfused_ms, 4),
             "unfused_us_per_call": round(unfused_ms * 1e3 / n_calls, 3),
             "graph_ms_per_step": round(graph_ms, 4),
@@ -387,7 +471,7 @@ def main():
         })
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.cpu_sample_calls)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_reps)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
