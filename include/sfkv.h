@@ -184,6 +184,24 @@ sfkv_status sfkv_write_attend(sfkv_cache *cache, const void *k, const void *v, c
                               sfkv_dtype dtype, int32_t n, float *out, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* sfkv_write_attend_noalloc: sfkv_write_attend with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Same kernels, same
+ * result bit for bit. The attend scratch (prepared query terms and split
+ * partials) is a library-owned static device array of
+ * SFKV_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, resolved once per device on the
+ * first call and held until the process ends; this call allocates nothing.
+ * Every call on one GPU shares that array and overwrites it (nothing in it
+ * needs to start at zero): calls that overlap on one GPU (different streams,
+ * or different threads without ordering) race and must not be issued.
+ * Errors: those of sfkv_write_attend; EINVAL also when the cache's
+ * configuration needs more scratch than the maximum (the production call,
+ * 24 x 128 with 757 new tokens of 5,788 slots, needs 23.4 MiB; 40 heads in
+ * bf16 storage 31.7 MiB), EHIP when the array's address cannot be resolved. */
+#define SFKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+sfkv_status sfkv_write_attend_noalloc(sfkv_cache *cache, const void *k, const void *v, const void *q,
+                                      sfkv_dtype dtype, int32_t n, float *out, void *stream);
+
 /* sfkv_rebase_positions: subtract delta from every position with one delta
  * rotation of the cached keys: each valid key's FP8 codes are rotated by
  * -delta*theta in the code domain (the per-head scale cancels), clamped and

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -119,6 +120,37 @@ sfkv_status launched(hipError_t e) {
 
 }  // namespace
 
+// ---- allocation-free variant of the fused call -------------------------------
+// The attend workspace (query terms and split partials) of sfkv_write_attend_
+// noalloc lives in this file-scope device array, one copy per GPU, held from the
+// first use of the library on that GPU until the process ends. Host code never
+// passes the array's name (a host-side stand-in) to a kernel: it resolves the
+// device address once per device with hipGetSymbolAddress and uses that.
+static __device__ __align__(256) uint8_t scratch[SFKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+sfkv_status scratch_of_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SFKV_EHIP, std::string("hipGetDevice failed: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SFKV_EINVAL, "device index beyond the library's device table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SFKV_EHIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SFKV_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char *sfkv_status_string(sfkv_status s) {
@@ -212,6 +244,10 @@ sfkv_status sfkv_cache_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, vo
   c->last_n = 0;
   c->cus = device_cus();
   c->calibrated = false;
+  // set-up of the allocation-free call's scratch on this device (resolved once
+  // per device; sfkv_write_attend_noalloc reports a failure itself)
+  void *unused = nullptr;
+  (void)scratch_of_current_device(&unused);
   *out = c;
   return ok();
 }
@@ -371,6 +407,24 @@ sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t 
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
   return attend_planes(c->cfg, c->cus, c->rope, c->base, n_valid_of(c), c->last_pos0, q, dtype, n_q, out,
                        workspace, workspace_bytes, stream);
+}
+
+sfkv_status sfkv_write_attend(sfkv_cache *c, const void *k, const void *v, const void *q, sfkv_dtype dtype,
+                              int32_t n, float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+sfkv_status sfkv_write_attend_noalloc(sfkv_cache *c, const void *k, const void *v, const void *q,
+                                      sfkv_dtype dtype, int32_t n, float *out, void *stream) {
+  if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  const size_t need = attend_ws(c->cfg, c->cus).total;
+  if (need > SFKV_NOALLOC_SCRATCH_BYTES)
+    return fail(SFKV_EINVAL, "this cache configuration needs " + std::to_string(need) +
+                                 " bytes of attend scratch, above the static maximum of " +
+                                 std::to_string(static_cast<size_t>(SFKV_NOALLOC_SCRATCH_BYTES)) +
+                                 "; use sfkv_write_attend with a workspace");
+  void *ws = nullptr;
+  const sfkv_status st = scratch_of_current_device(&ws);
+  if (st != SFKV_OK) return st;
+  return sfkv_write_attend(c, k, v, q, dtype, n, out, ws, SFKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 sfkv_status sfkv_write_attend(sfkv_cache *c, const void *k, const void *v, const void *q, sfkv_dtype dtype,

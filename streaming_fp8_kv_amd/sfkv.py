@@ -8,8 +8,8 @@ is no fallback implementation.
 The function names mirror the C entry points without their ``sfkv_`` prefix:
 ``rope_bytes``, ``rope_init``, ``cache_bytes``, ``cache_init``,
 ``calibrate_scales``, ``cache_write``, ``attend_workspace_bytes``, ``attend``,
-``write_attend``, ``rebase_positions``, ``rebase_positions_many``,
-``cache_state``, ``cache_layout``, and for the launch
+``write_attend``, ``write_attend_noalloc``, ``rebase_positions``,
+``rebase_positions_many``, ``cache_state``, ``cache_layout``, and for the launch
 software's plain linear window ``linear_bytes``, ``linear_init``,
 ``linear_calibrate_scales``, ``linear_write``, ``linear_workspace_bytes``,
 ``linear_attend``, ``linear_state``, ``linear_layout``. ``Rope``,
@@ -40,7 +40,7 @@ SYMBOLS = (
     "sfkv_cache_bytes", "sfkv_cache_init", "sfkv_cache_destroy",
     "sfkv_calibrate_scales", "sfkv_cache_write",
     "sfkv_attend_workspace_bytes", "sfkv_attend", "sfkv_write_attend", "sfkv_rebase_positions",
-    "sfkv_rebase_positions_many",
+    "sfkv_rebase_positions_many", "sfkv_write_attend_noalloc",
     "sfkv_cache_state", "sfkv_cache_layout",
     "sfkv_linear_bytes", "sfkv_linear_init", "sfkv_linear_destroy",
     "sfkv_linear_calibrate_scales", "sfkv_linear_write", "sfkv_linear_workspace_bytes",
@@ -80,6 +80,7 @@ _sig("sfkv_cache_write", ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i32, _vp)
 _sig("sfkv_attend_workspace_bytes", _sz, _vp)
 _sig("sfkv_attend", ctypes.c_int, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
 _sig("sfkv_write_attend", ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp)
+_sig("sfkv_write_attend_noalloc", ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _vp, _vp)
 _sig("sfkv_rebase_positions", ctypes.c_int, _vp, _i64, _vp)
 _sig("sfkv_rebase_positions_many", ctypes.c_int, _P(_vp), _P(_i64), _i32, _vp)
 _sig("sfkv_cache_state", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i32), _P(_i32))
@@ -184,6 +185,18 @@ def write_attend(handle: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.sfkv_write_attend(handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), code, k.shape[0],
                                   out.data_ptr(), ws_ptr, ws_len, _stream(stream)))
+
+
+def write_attend_noalloc(handle: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                         stream=None):
+    """write_attend with the library's static scratch instead of a workspace."""
+    code = _dtype_code(k)
+    if _dtype_code(v) != code or _dtype_code(q) != code:
+        raise ValueError("k, v and q must share one dtype")
+    if v.shape != k.shape or q.shape != k.shape:
+        raise ValueError("k, v and q must have one shape [n, heads, head_dim]")
+    _check(_lib.sfkv_write_attend_noalloc(handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), code, k.shape[0],
+                                          out.data_ptr(), _stream(stream)))
 
 
 def rebase_positions(handle: int, delta: int, stream=None):
