@@ -267,17 +267,24 @@ __device__ inline uint4 rebase_chunk(uint4 w, const RopePair *t) {
   }
 }
 
-// Delta rotation of the cached keys of up to kRebaseBatch caches in one
-// launch (a position reset of every cache of a step is one launch, not one per
-// cache). Work unit = (cache, head, block of rows); workgroups
-// stride over the units. In a unit each thread owns one 16-byte column chunk
-// of J rows of its wave's slab, loads all J before the first store, and
-// loads its chunk's cos/sin pairs once; the lanes of a wave cover 64 / (chunks
-// per row) consecutive rows completely at each step, so every load and store
-// is one contiguous kilobyte per wave. Rows at or past a cache's n_valid are
-// left alone. For head 0, chunk 0 also moves the slot's position by -delta.
-template <int D, int ST>
-__global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunch a) {
+// Delta rotation of the cached keys of up to NE caches in one launch (a
+// position reset of every cache of a step is one or two launches, not one per
+// cache). Work unit = (cache, head, block of rows); workgroups stride over the
+// units. In a unit each thread owns one 16-byte column chunk of J rows of its
+// wave's slab, loads all J before the first store, and loads its chunk's
+// cos/sin pairs once; the lanes of a wave cover 64 / (chunks per row)
+// consecutive rows completely at each step, so every load and store is one
+// contiguous kilobyte per wave. The planes are streamed once with no reuse, so
+// codes are loaded and stored non-temporally. Rows at or past a cache's
+// n_valid are left alone. For head 0, chunk 0 also moves the slot's position
+// by -delta.
+// Measured over the 240 production caches (8.53 GB read and written): 1.63 ms
+// against 1.61 ms for the same stream with the arithmetic replaced by an xor
+// (5.2 to 5.3 TB/s); 4 rows per thread and 16 workgroups per CU were the best
+// of 2, 4 or 8 rows and 4, 8 or 16 workgroups, non-temporal or not.
+typedef uint32_t v4u_nt __attribute__((ext_vector_type(4)));
+template <int D, int ST, int NE>
+__global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunchN<NE> a) {
   constexpr int ES = ST == kBF16 ? 2 : 1;       // bytes per element
   constexpr int CH = D * ES / 16;       // 16-byte chunks per row
   constexpr int PAIRS = 8 / ES;         // code pairs per 16-byte chunk
@@ -306,14 +313,20 @@ __global__ __launch_bounds__(256) void rebase_kernel(RebaseLaunch a) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int slot = slot0 + j * RSTEP;
-      if (slot < en.n_valid) w[j] = *reinterpret_cast<const uint4 *>(base + static_cast<size_t>(slot) * plane_row);
+      if (slot < en.n_valid) {
+        const v4u_nt x =
+            __builtin_nontemporal_load(reinterpret_cast<const v4u_nt *>(base + static_cast<size_t>(slot) * plane_row));
+        w[j] = uint4{x[0], x[1], x[2], x[3]};
+      }
     }
     int32_t *pos = reinterpret_cast<int32_t *>(en.base + a.pos_off);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int slot = slot0 + j * RSTEP;
       if (slot < en.n_valid) {
-        *reinterpret_cast<uint4 *>(base + static_cast<size_t>(slot) * plane_row) = rebase_chunk<ST>(w[j], t);
+        const uint4 o = rebase_chunk<ST>(w[j], t);
+        __builtin_nontemporal_store(v4u_nt{o.x, o.y, o.z, o.w},
+                                    reinterpret_cast<v4u_nt *>(base + static_cast<size_t>(slot) * plane_row));
         if (h == 0 && c == 0) pos[slot] -= en.delta;
       }
     }
@@ -387,22 +400,42 @@ hipError_t launch_calibrate(const CalibrateLaunch &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s, int cus) {
+template <int NE>
+hipError_t launch_rebase_n(const RebaseLaunchN<NE> &a, hipStream_t s, int cus) {
   if (a.count <= 0 || a.max_valid <= 0 || a.heads <= 0) return hipSuccess;
   const int es = a.storage == kBF16 ? 2 : 1;
   const int rows = 4 * (64 / (a.head_dim * es / 16)) * kRebaseRowsPerThread;
   const int64_t units = static_cast<int64_t>(a.count) * a.heads * ((a.max_valid + rows - 1) / rows);
-  // eight resident workgroups per CU stride over the units
-  const int64_t cap = 8 * static_cast<int64_t>(cus > 0 ? cus : 256);
+  // 16 workgroups per CU stride over the units (about half of them resident
+  // at a time)
+  const int64_t cap = 16 * static_cast<int64_t>(cus > 0 ? cus : 256);
   const dim3 grid(static_cast<unsigned>(units < cap ? units : cap));
   if (a.storage == kBF16) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((rebase_kernel<128, kBF16>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rebase_kernel<64, kBF16>), grid, dim3(256), 0, s, a);
+    if (a.head_dim == 128) hipLaunchKernelGGL((rebase_kernel<128, kBF16, NE>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rebase_kernel<64, kBF16, NE>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.head_dim == 128) hipLaunchKernelGGL((rebase_kernel<128, kE4M3>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rebase_kernel<64, kE4M3>), grid, dim3(256), 0, s, a);
+    if (a.head_dim == 128) hipLaunchKernelGGL((rebase_kernel<128, kE4M3, NE>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rebase_kernel<64, kE4M3, NE>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_rebase(const RebaseLaunch &a, hipStream_t s, int cus) {
+  if (a.count == 1) {
+    // one cache: a 64-byte argument block instead of the batch's 2 KB
+    RebaseLaunchN<1> one;
+    one.rope = a.rope;
+    one.pos_off = a.pos_off;
+    one.storage = a.storage;
+    one.heads = a.heads;
+    one.head_dim = a.head_dim;
+    one.capacity = a.capacity;
+    one.count = 1;
+    one.max_valid = a.max_valid;
+    one.entry[0] = a.entry[0];
+    return launch_rebase_n(one, s, cus);
+  }
+  return launch_rebase_n(a, s, cus);
 }
 
 }  // namespace sfkv

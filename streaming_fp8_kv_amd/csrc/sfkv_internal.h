@@ -36,11 +36,12 @@ struct CalibrateLaunch {
   float *scales;
 };
 
-// Delta rotation of the keys of up to kRebaseBatch caches of one
-// configuration (storage, heads, head_dim, capacity) and one RoPE table in one
-// launch. Each cache's buffer starts with its K plane (offset 0 of the cache
-// layout); its positions sit at pos_off. The whole argument block travels as
-// kernel arguments (2 KB), so a captured launch carries its own copy.
+// Delta rotation of the keys of up to NE caches of one configuration
+// (storage, heads, head_dim, capacity) and one RoPE table in one launch. Each
+// cache's buffer starts with its K plane (offset 0 of the cache layout); its
+// positions sit at pos_off. The argument block travels as kernel arguments
+// (about 2 KB for kRebaseBatch entries, 64 bytes for one), so a captured
+// launch carries its own copy.
 constexpr int kRebaseBatch = 128;
 constexpr int kRebaseRowsPerThread = 4;
 struct RebaseEntry {
@@ -48,14 +49,16 @@ struct RebaseEntry {
   int32_t n_valid;   // valid slots (rows 0 .. n_valid - 1 of every head)
   int32_t delta;     // rotation by -delta; positions drop by delta
 };
-struct RebaseLaunch {
+template <int NE>
+struct RebaseLaunchN {
   const RopePair *rope;      // the table, [max_position + 1][head_dim / 2]
   size_t pos_off;            // byte offset of positions[] in a cache's buffer
   int storage, heads, head_dim, capacity;
-  int count;                 // entries used
+  int count;                 // entries used, <= NE
   int max_valid;             // largest n_valid among them
-  RebaseEntry entry[kRebaseBatch];
+  RebaseEntry entry[NE];
 };
+using RebaseLaunch = RebaseLaunchN<kRebaseBatch>;
 
 struct AttendLaunch {
   int storage;
