@@ -222,7 +222,10 @@ sfkv_status sfkv_rebase_positions(sfkv_cache *cache, int64_t delta, void *stream
  * that share storage, num_heads, head_dim, capacity and RoPE table are rotated
  * together, up to 128 per kernel launch, so a reset of every cache of a step is
  * one or two launches rather than one per cache.
- * Errors: EINVAL (count < 0, NULL arrays or entries, a cache listed twice),
+ * The launches go to the current device, which must be the device every
+ * listed cache was set up on.
+ * Errors: EINVAL (count < 0, NULL arrays or entries, a cache listed twice, a
+ *         cache of another device),
  *         ERANGE (some deltas[i] < 0 or > next_pos of caches[i]); on either
  *         nothing is enqueued and no state changes. EHIP: the caches whose
  *         launch was enqueued before the failing one are rebased, the others

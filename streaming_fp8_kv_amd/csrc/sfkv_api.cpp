@@ -34,6 +34,7 @@ struct sfkv_cache {
   int64_t last_pos0;
   int32_t last_n;
   int cus;          // compute units of the device the cache was set up on
+  int device;       // that device's index
   bool calibrated;
 };
 
@@ -106,6 +107,11 @@ sfkv_status check_frame(const sfkv_cache *c, const void *k, const void *v, sfkv_
 
 // Compute units of the current device (the attention grid is planned for two
 // workgroups per CU); 256 if the runtime cannot say.
+int current_device() {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -243,6 +249,7 @@ sfkv_status sfkv_cache_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, vo
   c->last_pos0 = 0;
   c->last_n = 0;
   c->cus = device_cus();
+  c->device = current_device();
   c->calibrated = false;
   // set-up of the allocation-free call's scratch on this device (resolved once
   // per device; sfkv_write_attend_noalloc reports a failure itself)
@@ -515,6 +522,10 @@ sfkv_status sfkv_rebase_positions_many(sfkv_cache *const *caches, const int64_t 
     if (deltas[i] < 0 || deltas[i] > caches[i]->next_pos)
       return fail(SFKV_ERANGE, "deltas[" + std::to_string(i) + "] must be in [0, next_pos] of its cache");
   }
+  const int dev = current_device();
+  for (int32_t i = 0; i < count; ++i)
+    if (caches[i]->device != dev)
+      return fail(SFKV_EINVAL, "caches[" + std::to_string(i) + "] was set up on another device than the current one");
   std::vector<const sfkv_cache *> sorted(caches, caches + count);
   std::sort(sorted.begin(), sorted.end());
   if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
