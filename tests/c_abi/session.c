@@ -14,9 +14,12 @@
  * key plane and the value plane (heads * capacity * head_dim elements of the
  * storage's size), positions int32[capacity] and scales float32[4][heads].
  *
- * Frames 0, 2, 4, ... go through sfkv_cache_write + sfkv_attend, the others
- * through sfkv_write_attend. Frame 0 calibrates the scales. Every device
- * buffer is the caller's (hipMalloc here); every call runs on the null stream.
+ * Frame f goes through sfkv_cache_write + sfkv_attend when f % 3 == 0,
+ * through sfkv_write_attend when f % 3 == 1 and through
+ * sfkv_write_attend_noalloc (no workspace) when f % 3 == 2. Frame 0 calibrates
+ * the scales; the position reset goes through sfkv_rebase_positions_many with
+ * the one cache. Every device buffer is the caller's (hipMalloc here); every
+ * call runs on the null stream.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -118,13 +121,15 @@ int main(int argc, char **argv) {
     if (f == reset_before) {
       int64_t next_pos = 0;
       sfkv_ok(sfkv_cache_state(cache, NULL, &next_pos, NULL, NULL), "cache_state");
-      sfkv_ok(sfkv_rebase_positions(cache, next_pos, NULL), "rebase_positions");
+      sfkv_ok(sfkv_rebase_positions_many(&cache, &next_pos, 1, NULL), "rebase_positions_many");
     }
-    if (f % 2 == 0) {
+    if (f % 3 == 0) {
       sfkv_ok(sfkv_cache_write(cache, dk, dv, SFKV_FP32, n, NULL), "cache_write");
       sfkv_ok(sfkv_attend(cache, dq, SFKV_FP32, n, dout, ws, ws_bytes, NULL), "attend");
-    } else {
+    } else if (f % 3 == 1) {
       sfkv_ok(sfkv_write_attend(cache, dk, dv, dq, SFKV_FP32, n, dout, ws, ws_bytes, NULL), "write_attend");
+    } else {
+      sfkv_ok(sfkv_write_attend_noalloc(cache, dk, dv, dq, SFKV_FP32, n, dout, NULL), "write_attend_noalloc");
     }
     hip_ok(hipMemcpy(host, dout, bytes, hipMemcpyDeviceToHost), "copy output");
     write_exact(out, host, bytes);
