@@ -30,6 +30,13 @@
  *     nothing is enqueued and the cache state is unchanged; sfkv_last_error()
  *     returns a message for the calling thread.
  *   - Handles are not thread-safe; calls on one handle must be serialised.
+ *   - Calls may be captured into a HIP graph: kernel arguments (including the
+ *     host-mirrored ring state) are fixed at capture, and the host state
+ *     advances once, at capture. Replaying a captured write or attend redoes
+ *     the same work on the same slots and positions (the result is the same
+ *     every replay); replaying a captured rebase rotates the cached keys
+ *     again every time, so capture a rebase only where each replay stands for
+ *     one real reset and the host state is kept in step by the caller.
  *
  * Tensor layouts (row-major, contiguous, 16-byte aligned):
  *   Q, K, V inputs : [n_tokens][num_heads][head_dim], bf16 or fp32
