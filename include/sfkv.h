@@ -196,16 +196,18 @@ sfkv_status sfkv_write_attend(sfkv_cache *cache, const void *k, const void *v, c
  * tight serving loops, harnesses that forbid allocation). Same kernels, same
  * result bit for bit. The attend scratch (prepared query terms and split
  * partials) is a library-owned static device array of
- * SFKV_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, resolved once per device on the
- * first call and held until the process ends; this call allocates nothing.
+ * SFKV_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, resolved once per device when
+ * the first cache is set up there and held until the process ends; this call
+ * allocates nothing.
  * Every call on one GPU shares that array and overwrites it (nothing in it
  * needs to start at zero): calls that overlap on one GPU (different streams,
  * or different threads without ordering) race and must not be issued.
  * Errors: those of sfkv_write_attend; EINVAL also when the cache's
  * configuration needs more scratch than the maximum (the production call,
- * 24 x 128 with 757 new tokens of 5,788 slots, needs 23.4 MiB; 40 heads in
- * bf16 storage 31.7 MiB), EHIP when the array's address cannot be resolved. */
-#define SFKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+ * 24 x 128 with 757 new tokens of 5,788 slots, needs 23.4 MiB, 42.2 MiB in
+ * bf16 storage; 40 heads in bf16 storage 48.3 MiB), EHIP when the array's
+ * address cannot be resolved. */
+#define SFKV_NOALLOC_SCRATCH_BYTES (64u << 20)
 sfkv_status sfkv_write_attend_noalloc(sfkv_cache *cache, const void *k, const void *v, const void *q,
                                       sfkv_dtype dtype, int32_t n, float *out, void *stream);
 

@@ -163,18 +163,22 @@ __device__ inline int real_pair(int q, int n_pairs, int slo, int X) {
 // its L2 (workgroups are dealt to the 8 XCDs round-robin).
 //
 // ST selects the cache storage. kE4M3: raw E4M3 keys into the block-scaled FP8
-// MFMA with three query terms, two workgroups per CU. kBF16 (the non-FP8
-// variant): bf16 keys as stored into the bf16 MFMA 32x32x16 with two query
-// terms, and bf16 values moved into fp16 by the head's power-of-two factor;
-// a bf16 key tile is twice the size, so the three buffers leave room for one
-// workgroup per CU.
+// MFMA with three query terms; 4 waves (128 queries) per workgroup, two
+// workgroups per CU. kBF16 (the non-FP8 variant): bf16 keys as stored into the
+// bf16 MFMA 32x32x16 with two query terms, and bf16 values moved into fp16 by
+// the head's power-of-two factor; a bf16 key tile is twice the size, so the
+// three buffers leave room for one workgroup per CU, which therefore has 8
+// waves (256 queries) sharing every staged tile: two waves per SIMD (with 4
+// waves the bf16 attend call took 136 against 105 us at the production shape).
 template <int D, int ST>
-__global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(AttendLaunch a) {
+__global__ __launch_bounds__(attend_threads(ST), ST == kE4M3 ? 2 : 1) void attend_kernel(AttendLaunch a) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr bool BF = ST == kBF16;
   constexpr int ES = BF ? 2 : 1;      // bytes per stored element
   constexpr int DH = D / 64;          // 64-dim halves of the head
-  constexpr int BQB = 128;            // queries per workgroup
+  constexpr int NTH = attend_threads(ST);            // 256 (E4M3) or 512 (bf16)
+  constexpr int BQB = attend_queries_per_block(ST);  // queries per workgroup: 32 per wave
+  constexpr int VR = 1024 / NTH;                     // V rows a thread stages per tile
   constexpr float kShiftAt = 15.0f;   // P = exp2(s - m_ref) stays <= 2^15, inside fp16
   constexpr int KROW = BF ? 2 * D + 16 : KSTRIDE;   // bytes per key row in LDS
   __shared__ __attribute__((aligned(16))) uint8_t sK[3][BK * KROW];
@@ -242,8 +246,8 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
   // buffer descriptors whose size ends at this workgroup's last key, so rows
   // past the range read as zeros without touching memory; the per-thread offset
   // is fixed and the tile start is the scalar offset.
-  constexpr int KPASS = (BK * D * ES / 16) / 256;
-  static_assert(!(BF && D == 128) || KPASS == 4, "the bf16 staging spread places four K chunks per thread");
+  constexpr int KPASS = (BK * D * ES / 16) / NTH;
+  static_assert(!(BF && D == 128) || (KPASS == 2 && VR == 2), "the bf16 staging spread places two V rows and two K chunks per thread");
   constexpr int KCH = D * ES / 16;         // 16-byte chunks per key row
   constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor, gfx9 family
   const int v_dg = tid & 15, v_kq = tid >> 4;
@@ -259,13 +263,13 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
   int koff[KPASS];
 #pragma unroll
   for (int p = 0; p < KPASS; ++p) {
-    const int c = tid + p * 256;
+    const int c = tid + p * NTH;
     koff[p] = (c / KCH) * D * ES + 16 * (c % KCH);
   }
-  const int voff = (4 * v_kq * D + 8 * v_dg) * ES;
+  const int voff = (VR * v_kq * D + 8 * v_dg) * ES;
   uint4 pk[KPASS];
-  uint2 pv[4];
-  uint4 pvb[4];      // bf16 values: 8 dims of one key per load
+  uint2 pv[VR];
+  uint4 pvb[VR];     // bf16 values: 8 dims of one key per load
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
       pk[p] = uint4{w[0], w[1], w[2], w[3]};
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < VR; ++j) {
       if constexpr (BF) {
         auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + j * D * ES, kt * D * ES, 0);
         pvb[j] = uint4{w[0], w[1], w[2], w[3]};
@@ -289,16 +293,16 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
   auto store_k = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      const int c = tid + p * 256, key = c / KCH, col = c % KCH;
+      const int c = tid + p * NTH, key = c / KCH, col = c % KCH;
       *reinterpret_cast<uint4 *>(sK[buf] + key * KROW + 16 * col) = pk[p];
     }
   };
   // one chunk of the same (the bf16 loop spreads them over its MFMAs)
   auto store_k1 = [&](int buf, int p) {
-    const int c = tid + p * 256, key = c / KCH, col = c % KCH;
+    const int c = tid + p * NTH, key = c / KCH, col = c % KCH;
     *reinterpret_cast<uint4 *>(sK[buf] + key * KROW + 16 * col) = pk[p];
   };
-  // row 4 v_kq + j has (row & 3) == j; the fp8 -> fp16 widening happens right
+  // row VR v_kq + j (with VR = 4, (row & 3) == j); the fp8 -> fp16 widening happens right
   // before the store, so only the loaded codes stay live between the phases
   auto store_v = [&](int buf, int j) __attribute__((always_inline)) {
     if (v_role) {
@@ -323,7 +327,8 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
         w16 = uint4{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
                     __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
       }
-      *reinterpret_cast<uint4 *>(sV[buf] + (4 * v_kq + j) * D + 8 * vchunk<D>(j, v_dg)) = w16;
+      const int vrow = VR * v_kq + j;
+      *reinterpret_cast<uint4 *>(sV[buf] + vrow * D + 8 * vchunk<D>(VR == 4 ? j : vrow, v_dg)) = w16;
     }
   };
 
@@ -491,15 +496,14 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
 #pragma unroll
         for (int pr = first[i]; pr < first[i + 1]; ++pr) exp2p(s_cur, 2 * pr, pw + pr);
       } else if constexpr (NQK == 16) {
-        // bf16 keys at d = 128 (one wave per SIMD, so the vector work has only
-        // this wave's MFMAs to hide behind): one weight pair behind every even
-        // score MFMA (2.5% faster per bf16 attend call than four groups of
-        // four behind the first four), and the staging of the next tile
-        // behind the odd ones, V rows behind 1, 3, 5, 7 and K chunks behind
-        // 9, 11, 13, 15 (2.2% faster than after the score and P V MFMAs)
+        // bf16 keys at d = 128: one weight pair behind every even score MFMA
+        // (2.5% faster per bf16 attend call than four groups of four behind
+        // the first four, measured with one wave per SIMD), and the staging
+        // of the next tile behind the odd ones: this thread's two V rows
+        // behind 1 and 3, its two K chunks behind 9 and 11
         if (i % 2 == 0) exp2p(s_cur, i, pw + i / 2);
-        if (stage && i % 2 == 1 && i < 8) store_v(sbuf, i / 2);
-        if (stage && i % 2 == 1 && i >= 8) store_k1(sbuf, (i - 8) / 2);
+        if (stage && i % 2 == 1 && i < 2 * VR) store_v(sbuf, i / 2);
+        if (stage && i % 2 == 1 && i >= 8 && (i - 8) / 2 < KPASS) store_k1(sbuf, (i - 8) / 2);
       } else {
         if (i < 4) exp4(s_cur, 4 * i, pw + 2 * i);
       }
@@ -523,13 +527,13 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db], pb0, oacc[db], 0, 0, 0);
-      if (NQK != 16 && stage && db < 4) store_v(sbuf, db);
+      if (NQK != 16 && stage && db < VR) store_v(sbuf, db);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db], pb1, oacc[db], 0, 0, 0);
-      if (NQK != 16 && stage && NDB + db < 4) store_v(sbuf, NDB + db);
+      if (NQK != 16 && stage && NDB + db < VR) store_v(sbuf, NDB + db);
       if (db == NDB - 1) tmax_next = block_max(s_next);   // in the shadow of the PV MFMAs
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(256, ST == kE4M3 ? 2 : 1) void attend_kernel(Attend
     load_tile(kbeg);
     store_k(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store_v(0, j);
+    for (int j = 0; j < VR; ++j) store_v(0, j);
     load_tile(kbeg + BK);                          // past the range reads zeros
     __syncthreads();
     v16f s0, s1;
@@ -641,7 +645,7 @@ __device__ inline void add8(float acc[8], float w, uint4 o) {
 
 template <int D, int NS>
 __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
-  constexpr int BQB = kAttendQueriesPerBlock;
+  const int BQB = attend_queries_per_block(a.storage);
   constexpr int RPB = 256 / (D / 8);           // rows per workgroup
   // workgroup -> (pair, chunk of RPB rows) on the XCD whose attention
   // workgroups took the pair's first key range (its split partials sit in
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
   // small pairs [ps0, ps1)
   const int pb0 = (b0 + slo - 1) / slo, pb1 = (b1 + slo - 1) / slo;
   const int ps0 = (q0 + slo) / (slo + 1), ps1 = (q1 + slo) / (slo + 1);
-  constexpr int CH = BQB / RPB;                 // chunks per pair
+  const int CH = BQB / RPB;                     // chunks per pair
   const int nbig = pb1 - pb0, nsmall = ps1 - ps0;
   const int chunk = jl % CH, k = jl / CH;
   int pair;
@@ -716,7 +720,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendLaunch a) {
 template <int D>
 void launch_combine(const AttendLaunch &a, hipStream_t st) {
   // the largest number of pairs any XCD owns, times the chunks of a pair
-  const int tiles_q = (a.n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock;
+  const int qpb = attend_queries_per_block(a.storage);
+  const int tiles_q = (a.n_q + qpb - 1) / qpb;
   const int n_pairs = tiles_q * a.heads;
   const int slo = a.split_lo, X = a.split_x;
   const int NB = (n_pairs - X) * slo, NSm = X * (slo + 1);
@@ -726,7 +731,7 @@ void launch_combine(const AttendLaunch &a, hipStream_t st) {
     const int n = (b1 + slo - 1) / slo - (b0 + slo - 1) / slo + (q1 + slo) / (slo + 1) - (q0 + slo) / (slo + 1);
     owned = n > owned ? n : owned;
   }
-  const int chunks = kAttendQueriesPerBlock / (256 / (D / 8));
+  const int chunks = qpb / (256 / (D / 8));
   const dim3 grid(static_cast<unsigned>(8 * owned * chunks));
   const int most = a.split_lo + (a.split_x > 0 ? 1 : 0);
   if (most <= 2) hipLaunchKernelGGL((combine_kernel<D, 2>), grid, dim3(256), 0, st, a);
@@ -737,9 +742,10 @@ void launch_combine(const AttendLaunch &a, hipStream_t st) {
 
 }  // namespace
 
-AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus) {
-  // about two workgroups per CU, each key range at least four tiles long
-  const int64_t pairs = static_cast<int64_t>((n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock) * heads;
+AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus, int qpb) {
+  // twice as many workgroups as CUs (two resident per CU with E4M3 storage,
+  // two rounds of one with bf16), each key range at least four tiles long
+  const int64_t pairs = static_cast<int64_t>((n_q + qpb - 1) / qpb) * heads;
   const int64_t nt = (n_valid + BK - 1) / BK;
   const int64_t max_split = nt / 4 > 1 ? nt / 4 : 1;
   int64_t g = 2 * static_cast<int64_t>(cus > 0 ? cus : 256);
@@ -753,7 +759,9 @@ AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus) {
 }
 
 hipError_t launch_attend(const AttendLaunch &a, hipStream_t st) {
-  const int tiles_q = (a.n_q + kAttendQueriesPerBlock - 1) / kAttendQueriesPerBlock;
+  const int qpb = attend_queries_per_block(a.storage);
+  const dim3 block(attend_threads(a.storage));
+  const int tiles_q = (a.n_q + qpb - 1) / qpb;
   const int n_pairs = tiles_q * a.heads;
   const int NB = (n_pairs - a.split_x) * a.split_lo, NS = a.split_x * (a.split_lo + 1);
   const int per_xcd = (NB + 7) / 8 + (NS + 7) / 8;   // largest XCD share
@@ -765,20 +773,20 @@ hipError_t launch_attend(const AttendLaunch &a, hipStream_t st) {
   if (a.storage == kBF16) {
     if (a.head_dim == 128) {
       if (prep) hipLaunchKernelGGL(query_prep_bf16_kernel<128>, prep_grid, dim3(256), 0, st, a);
-      hipLaunchKernelGGL((attend_kernel<128, kBF16>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attend_kernel<128, kBF16>), grid, block, 0, st, a);
       if (merge) launch_combine<128>(a, st);
     } else {
       if (prep) hipLaunchKernelGGL(query_prep_bf16_kernel<64>, prep_grid, dim3(256), 0, st, a);
-      hipLaunchKernelGGL((attend_kernel<64, kBF16>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attend_kernel<64, kBF16>), grid, block, 0, st, a);
       if (merge) launch_combine<64>(a, st);
     }
   } else if (a.head_dim == 128) {
     if (prep) hipLaunchKernelGGL(query_prep_kernel<128>, prep_grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((attend_kernel<128, kE4M3>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_kernel<128, kE4M3>), grid, block, 0, st, a);
     if (merge) launch_combine<128>(a, st);
   } else {
     if (prep) hipLaunchKernelGGL(query_prep_kernel<64>, prep_grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((attend_kernel<64, kE4M3>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_kernel<64, kE4M3>), grid, block, 0, st, a);
     if (merge) launch_combine<64>(a, st);
   }
   return hipGetLastError();

@@ -330,7 +330,8 @@ static int n_valid_of(const sfkv_cache *c) {
 //   query terms   [max_new][heads][3][head_dim] bytes (E4M3 storage) or
 //                 [max_new][heads][2][head_dim] bf16 (bf16 storage)
 //   query scales  [max_new][heads][head_dim/32] words
-//   split partials: O / l rows [workers][128][head_dim] fp16, then (max, sum)
+//   split partials: O / l rows [workers][queries per block][head_dim] fp16,
+//                 then (max, sum)
 struct AttendWs {
   size_t qterm, qscale, part_o, part_ml, total, slots;
 };
@@ -338,8 +339,9 @@ struct AttendWs {
 static AttendWs attend_ws(const sfkv_cache_cfg &cfg, int cus) {
   AttendWs w;
   const size_t qh = static_cast<size_t>(cfg.max_new_tokens) * cfg.num_heads;
-  w.slots = static_cast<size_t>(sfkv::attend_plan(cfg.max_new_tokens, cfg.num_heads, cfg.capacity, cus).workers);
-  const size_t rows = w.slots * sfkv::kAttendQueriesPerBlock;
+  const int qpb = sfkv::attend_queries_per_block(storage_of(cfg));
+  w.slots = static_cast<size_t>(sfkv::attend_plan(cfg.max_new_tokens, cfg.num_heads, cfg.capacity, cus, qpb).workers);
+  const size_t rows = w.slots * qpb;
   w.qterm = 0;
   w.qscale = align_up(qh * (cfg.storage == SFKV_STORE_BF16 ? 4 : 3) * cfg.head_dim, 256);
   w.part_o = align_up(w.qscale + qh * (cfg.head_dim / 32) * sizeof(uint32_t), 256);
@@ -368,7 +370,8 @@ static sfkv_status attend_setup(const sfkv_cache_cfg &cfg, int cus, const sfkv_r
   const Layout l = layout_of(cfg);
   // n_q <= max_new and nv <= capacity, so the plan never needs more partial
   // slots than the workspace holds; checked anyway
-  const sfkv::AttendPlan plan = sfkv::attend_plan(n_q, cfg.num_heads, nv, cus);
+  const sfkv::AttendPlan plan =
+      sfkv::attend_plan(n_q, cfg.num_heads, nv, cus, sfkv::attend_queries_per_block(storage_of(cfg)));
   if (static_cast<size_t>(plan.workers) > ws.slots)
     return fail(SFKV_EINVAL, "attend plan exceeds the workspace (n_q or n_valid above the configured sizes)");
   a.storage = storage_of(cfg);

@@ -72,8 +72,8 @@ struct AttendLaunch {
   float *out;
   int workers;               // attention workgroups (see AttendPlan)
   int split_lo, split_x;     // the plan's s_lo and x
-  uint16_t *part_o;          // [workers][128 rows][head_dim] fp16 split partials, O / l
-  float *part_ml;            // [workers][128 rows][2] (max, sum)
+  uint16_t *part_o;          // [workers][queries per block][head_dim] fp16 split partials, O / l
+  float *part_ml;            // [workers][queries per block][2] (max, sum)
   uint8_t *qterm;            // [n_q][heads][3][head_dim] E4M3 query terms
   uint32_t *qscale;          // [n_q][heads][head_dim/32] E8M0 scales, byte t = term t
 };
@@ -98,8 +98,13 @@ hipError_t launch_attend(const AttendLaunch &a, hipStream_t s);
 // queries), with q.queries_ready ignored.
 hipError_t launch_write_prep(const WriteLaunch &w, const AttendLaunch &q, hipStream_t s);
 
-// Attention tiling shared by the launcher and the workspace sizing.
-constexpr int kAttendQueriesPerBlock = 128;  // 4 waves x 32 queries
+// Attention tiling shared by the launcher and the workspace sizing. A wave
+// owns 32 queries. E4M3 storage: 4 waves (128 queries) per workgroup, two
+// workgroups per CU. bf16 storage: its key tiles are twice the size, so one
+// workgroup fits a CU; it has 8 waves (256 queries) sharing each staged tile,
+// which keeps two waves on every SIMD.
+constexpr int attend_threads(int storage) { return storage == kBF16 ? 512 : 256; }
+constexpr int attend_queries_per_block(int storage) { return attend_threads(storage) / 2; }
 constexpr int kAttendKeysPerTile = 64;
 // Work plan of one attend launch. The (head, 128-query tile) pairs are split
 // along the keys: the first `x` pairs into s_lo + 1 ranges ("small" ranges),
@@ -109,6 +114,6 @@ constexpr int kAttendKeysPerTile = 64;
 struct AttendPlan {
   int workers, s_lo, x;
 };
-AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus);
+AttendPlan attend_plan(int n_q, int heads, int n_valid, int cus, int queries_per_block);
 
 }  // namespace sfkv

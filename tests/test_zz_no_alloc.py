@@ -101,8 +101,8 @@ def test_noalloc_second_cache_and_oracle(sfkv):
 def test_noalloc_rejects_configurations_beyond_the_maximum(sfkv):
     say("case write_attend_noalloc size limit")
     rope = sfkv.Rope(128, 4096)
-    big = sfkv.RingCache(rope, 96, 4096, 2048)          # workspace far above 32 MiB
-    assert big.workspace_bytes() > (32 << 20)
+    big = sfkv.RingCache(rope, 96, 4096, 2048)          # workspace far above 64 MiB
+    assert big.workspace_bytes() > (64 << 20)
     x = torch.randn(16, 96, 128, device="cuda", dtype=torch.bfloat16)
     big.calibrate_scales(x, x)
     before = big.state()
