@@ -72,13 +72,16 @@ def profiled_attend_traffic():
         lines = open(TRAFFIC_PROFILE).read().splitlines()
     except OSError:
         return None, "no traffic profile"
-    recs = [json.loads(ln.split("bench-record:", 1)[1]) for ln in lines if ln.startswith("bench-record:")]
-    if not recs:
-        return None, "no bench-record line in the traffic profile"
-    rec = recs[-1]
-    if rec.get("sources_sha256") != attend_sources_sha256():
-        return None, "attend sources changed since the counters were taken"
-    return float(rec["attend_call_bytes"]), rec
+    try:
+        recs = [json.loads(ln.split("bench-record:", 1)[1]) for ln in lines if ln.startswith("bench-record:")]
+        if not recs:
+            return None, "no bench-record line in the traffic profile"
+        rec = recs[-1]
+        if rec.get("sources_sha256") != attend_sources_sha256():
+            return None, "attend sources changed since the counters were taken"
+        return float(rec["attend_call_bytes"]), rec
+    except (ValueError, KeyError, TypeError, OSError) as e:
+        return None, f"unreadable traffic record: {e}"
 
 
 def parse():

@@ -22,3 +22,26 @@ def test_help_lists_the_contract_flags():
     assert r.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup"):
         assert flag in r.stdout
+
+
+def test_traffic_record_is_used_only_for_the_profiled_sources(tmp_path, monkeypatch):
+    """roofline.traffic comes from the committed counter summary's record only
+    while the attention sources hash to the value it names; a stale or
+    unreadable record gives null with the reason."""
+    sys.path.insert(0, ROOT)
+    import bench
+    prof = tmp_path / "traffic.md"
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
+    good = {"sources_sha256": bench.attend_sources_sha256(), "attend_call_bytes": 123456789,
+            "fetch_factor": 2.0, "taken": "test"}
+    prof.write_text("# summary\n\nbench-record: " + json.dumps(good) + "\n")
+    value, rec = bench.profiled_attend_traffic()
+    assert value == 123456789.0 and rec["taken"] == "test"
+    prof.write_text("bench-record: " + json.dumps(dict(good, sources_sha256="0" * 64)) + "\n")
+    value, why = bench.profiled_attend_traffic()
+    assert value is None and "changed" in why
+    prof.write_text("bench-record: {not json\n")
+    value, why = bench.profiled_attend_traffic()
+    assert value is None and "unreadable" in why
+    prof.write_text("no record here\n")
+    assert bench.profiled_attend_traffic()[0] is None
