@@ -42,6 +42,12 @@ import time
 # MI355X published peaks
 PEAK_FP8_TFLOPS = 5000.0      # dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
+# Device-side spin enqueued ahead of a timed pass of short launches (cache
+# writes of about 6 us, single-cache rebases of about 10 us): the host queues
+# the whole pass while the GPU spins (several ms at any shader clock), so the
+# two events around the pass time the GPU's back-to-back execution and not the
+# host's issue rate.
+HEAD_START_CYCLES = 20_000_000
 
 # HBM traffic of one attend call (query prep + attention + merge) comes from
 # two rocprofv3 --pmc passes over this benchmark (FETCH_SIZE scaled by the
@@ -223,6 +229,7 @@ def plain_path(sfkv, W, spec, n_caches: int, stream):
     # two events (each attend uses its own cache's write)
     e0, e1, e2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(HEAD_START_CYCLES)
     e0.record(stream)
     for c, (q, k, v) in zip(caches, last):
         c.cache_write(k, v, stream)
@@ -348,6 +355,7 @@ def main():
     # ---- cache_write alone: one step's worth back to back between two events ----
     w0, w1 = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(HEAD_START_CYCLES)
     w0.record(stream)
     for c, (q, k, v) in zip(sw.caches, sw.frames):
         sfkv.cache_write(c.handle, k, v, stream)
@@ -384,6 +392,7 @@ def main():
     # work. ----
     r0, r1 = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(HEAD_START_CYCLES)
     r0.record(stream)
     for c in sw.caches:
         c.rebase_positions(c.state()["next_pos"] // 3, stream)

@@ -129,6 +129,40 @@ def _frame(t: torch.Tensor, heads: int, head_dim: int) -> torch.Tensor:
     return t
 
 
+# The library sees only pointers: it reads every input with the first one's
+# dtype and row count and writes n_q * heads * head_dim floats to out, so the
+# binding refuses tensors that would let a kernel read or write past an end.
+def _device_buf(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous CUDA tensor")
+    return t
+
+
+def _same_frame(first: torch.Tensor, *others: torch.Tensor):
+    for t in (first,) + others:
+        _device_buf(t, "every input")
+        if t.dim() != 3:
+            raise ValueError("inputs must have shape [n, heads, head_dim]")
+    for t in others:
+        if t.dtype != first.dtype or t.shape != first.shape or t.device != first.device:
+            raise ValueError("inputs of one call must share one dtype, shape [n, heads, head_dim] and device")
+
+
+def _out_for(out: torch.Tensor, q: torch.Tensor):
+    _device_buf(out, "out")
+    if out.dtype != torch.float32 or out.shape != q.shape or out.device != q.device:
+        raise ValueError("out must be a float32 tensor of q's shape on q's device")
+
+
+def _workspace(ws: Optional[torch.Tensor], q: torch.Tensor):
+    if ws is None:
+        return None, 0
+    _device_buf(ws, "workspace")
+    if ws.device != q.device:
+        raise ValueError("workspace must be on q's device")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 # ---- C entry points -----------------------------------------------------------
 def rope_bytes(head_dim: int, max_position: int) -> int:
     return int(_lib.sfkv_rope_bytes(head_dim, max_position))
@@ -136,6 +170,7 @@ def rope_bytes(head_dim: int, max_position: int) -> int:
 
 def rope_init(base: float, head_dim: int, max_position: int, buf: torch.Tensor, stream=None) -> int:
     h = _vp()
+    _device_buf(buf, "buf")
     _check(_lib.sfkv_rope_init(base, head_dim, max_position, buf.data_ptr(), buf.numel(),
                                _stream(stream), ctypes.byref(h)))
     return h.value
@@ -147,17 +182,20 @@ def cache_bytes(cfg: CacheConfig) -> int:
 
 def cache_init(cfg: CacheConfig, rope_handle: int, buf: torch.Tensor, stream=None) -> int:
     h = _vp()
+    _device_buf(buf, "buf")
     _check(_lib.sfkv_cache_init(ctypes.byref(cfg), rope_handle, buf.data_ptr(), buf.numel(),
                                 _stream(stream), ctypes.byref(h)))
     return h.value
 
 
 def calibrate_scales(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _same_frame(k, v)
     _check(_lib.sfkv_calibrate_scales(handle, k.data_ptr(), v.data_ptr(), _dtype_code(k),
                                       k.shape[0], _stream(stream)))
 
 
 def cache_write(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _same_frame(k, v)
     _check(_lib.sfkv_cache_write(handle, k.data_ptr(), v.data_ptr(), _dtype_code(k),
                                  k.shape[0], _stream(stream)))
 
@@ -168,8 +206,9 @@ def attend_workspace_bytes(handle: int) -> int:
 
 def attend(handle: int, q: torch.Tensor, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
            stream=None):
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _same_frame(q)
+    _out_for(out, q)
+    ws_ptr, ws_len = _workspace(workspace, q)
     _check(_lib.sfkv_attend(handle, q.data_ptr(), _dtype_code(q), q.shape[0], out.data_ptr(),
                             ws_ptr, ws_len, _stream(stream)))
 
@@ -177,12 +216,9 @@ def attend(handle: int, q: torch.Tensor, out: torch.Tensor, workspace: Optional[
 def write_attend(handle: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
                  workspace: Optional[torch.Tensor] = None, stream=None):
     code = _dtype_code(k)
-    if _dtype_code(v) != code or _dtype_code(q) != code:
-        raise ValueError("k, v and q must share one dtype")
-    if v.shape != k.shape or q.shape != k.shape:
-        raise ValueError("k, v and q must have one shape [n, heads, head_dim]")
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _same_frame(k, v, q)
+    _out_for(out, q)
+    ws_ptr, ws_len = _workspace(workspace, q)
     _check(_lib.sfkv_write_attend(handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), code, k.shape[0],
                                   out.data_ptr(), ws_ptr, ws_len, _stream(stream)))
 
@@ -191,10 +227,8 @@ def write_attend_noalloc(handle: int, k: torch.Tensor, v: torch.Tensor, q: torch
                          stream=None):
     """write_attend with the library's static scratch instead of a workspace."""
     code = _dtype_code(k)
-    if _dtype_code(v) != code or _dtype_code(q) != code:
-        raise ValueError("k, v and q must share one dtype")
-    if v.shape != k.shape or q.shape != k.shape:
-        raise ValueError("k, v and q must have one shape [n, heads, head_dim]")
+    _same_frame(k, v, q)
+    _out_for(out, q)
     _check(_lib.sfkv_write_attend_noalloc(handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), code, k.shape[0],
                                           out.data_ptr(), _stream(stream)))
 
@@ -231,16 +265,19 @@ def linear_bytes(cfg: CacheConfig, dtype: int) -> int:
 
 def linear_init(cfg: CacheConfig, rope_handle: int, dtype: int, buf: torch.Tensor, stream=None) -> int:
     h = _vp()
+    _device_buf(buf, "buf")
     _check(_lib.sfkv_linear_init(ctypes.byref(cfg), rope_handle, dtype, buf.data_ptr(), buf.numel(),
                                  _stream(stream), ctypes.byref(h)))
     return h.value
 
 
 def linear_calibrate_scales(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _same_frame(k, v)
     _check(_lib.sfkv_linear_calibrate_scales(handle, k.data_ptr(), v.data_ptr(), k.shape[0], _stream(stream)))
 
 
 def linear_write(handle: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    _same_frame(k, v)
     _check(_lib.sfkv_linear_write(handle, k.data_ptr(), v.data_ptr(), k.shape[0], _stream(stream)))
 
 
@@ -249,8 +286,11 @@ def linear_workspace_bytes(handle: int) -> int:
 
 
 def linear_attend(handle: int, q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor, stream=None):
-    _check(_lib.sfkv_linear_attend(handle, q.data_ptr(), q.shape[0], out.data_ptr(), workspace.data_ptr(),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    _same_frame(q)
+    _out_for(out, q)
+    ws_ptr, ws_len = _workspace(workspace, q)
+    _check(_lib.sfkv_linear_attend(handle, q.data_ptr(), q.shape[0], out.data_ptr(), ws_ptr, ws_len,
+                                   _stream(stream)))
 
 
 def linear_state(handle: int) -> dict:

@@ -1,7 +1,8 @@
 """C-ABI behaviour on the GPU: error statuses with the state left unchanged, the
 E4M3 encoder at every rounding boundary through the real write kernel, chained
 calls replayed from a captured graph, no host synchronisation in the per-step
-path, and no allocation keyed by token count."""
+path, no allocation keyed by token count, and the binding's refusal of tensors
+that would let a kernel read or write past an end."""
 import numpy as np
 import pytest
 import torch
@@ -62,6 +63,15 @@ def test_errors_leave_state_unchanged(sfkv, rope128):
     with pytest.raises(sfkv.SfkvError) as e:
         c2.cache_write(x, x)
     assert e.value.status == sfkv.ERANGE and c2.state() == st
+    # an empty frame: n_tokens must be at least 1
+    empty = x[:0]
+    for call in (lambda: c.cache_write(empty, empty), lambda: c.calibrate_scales(empty, empty)):
+        with pytest.raises(sfkv.SfkvError) as e:
+            call()
+        assert e.value.status == sfkv.EINVAL and c.state() == before
+    # an empty batched reset changes nothing
+    sfkv.rebase_positions_many([], [])
+    assert c.state() == before
     # a workspace that is too small
     c3 = sfkv.RingCache(sfkv.Rope(128, 8192), 24, 5788, 757)
     need = c3.workspace_bytes()
@@ -241,3 +251,40 @@ def test_variable_first_lengths_allocate_nothing(sfkv):
         c.attend(x, out=outs[n], workspace=ws)
         torch.cuda.synchronize()
         assert torch.cuda.mem_get_info()[0] == free0
+
+
+def test_binding_refuses_mismatched_tensors(sfkv, rope128):
+    """The library reads every input with k's (or q's) dtype and row count and
+    writes n_q rows of float32 to out: the binding refuses a v, q, out or
+    workspace that does not match, before anything is launched."""
+    say("case binding argument checks")
+    c = sfkv.RingCache(rope128, 2, 64, 16)
+    x = torch.randn(8, 2, 128, device="cuda", dtype=torch.bfloat16)
+    c.calibrate_scales(x, x)
+    c.cache_write(x, x)
+    before = c.state()
+    short, wide = x[:4].contiguous(), x.float()
+    for k, v in ((x, short), (short, x), (x, wide), (wide, x), (x, x.cpu()), (x, x.transpose(0, 1))):
+        for call in (c.cache_write, c.calibrate_scales):
+            with pytest.raises(ValueError):
+                call(k, v)
+    ws = torch.empty(max(c.workspace_bytes(), 256), dtype=torch.uint8, device="cuda")
+    bad_outs = [torch.empty(4, 2, 128, device="cuda"), torch.empty(8, 2, 128, device="cuda", dtype=torch.bfloat16),
+                torch.empty(8, 2, 128), torch.empty(2, 8, 128, device="cuda").transpose(0, 1)]
+    for o in bad_outs:
+        with pytest.raises(ValueError):
+            c.attend(x, out=o, workspace=ws)
+        with pytest.raises(ValueError):
+            c.write_attend(x, x, x, out=o, workspace=ws)
+        with pytest.raises(ValueError):
+            sfkv.write_attend_noalloc(c.handle, x, x, x, o)
+    with pytest.raises(ValueError):
+        c.attend(x, workspace=ws.cpu())
+    with pytest.raises(ValueError):
+        c.write_attend(x, x, wide, workspace=ws)
+    torch.cuda.synchronize()
+    assert c.state() == before
+    # the same cache still works after the refusals
+    out = c.attend(x, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
