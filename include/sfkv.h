@@ -29,6 +29,8 @@
  *   - Validation happens on the host before anything is enqueued. On any error
  *     nothing is enqueued and the cache state is unchanged; sfkv_last_error()
  *     returns a message for the calling thread.
+ *   - Kernels are launched on the current HIP device, which must be the device
+ *     that was current when the handle was set up (EINVAL otherwise).
  *   - Handles are not thread-safe; calls on one handle must be serialised.
  *   - Calls may be captured into a HIP graph: kernel arguments (including the
  *     host-mirrored ring state) are fixed at capture, and the host state

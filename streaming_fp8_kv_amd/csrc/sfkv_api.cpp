@@ -93,9 +93,25 @@ sfkv_status check_cfg(const sfkv_cache_cfg *c) {
   return SFKV_OK;
 }
 
+int current_device() {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
+// Kernels launch on the current device; a handle's device memory lives on the
+// device that was current when it was set up.
+sfkv_status check_device(int dev) {
+  const int cur = current_device();
+  if (cur != dev)
+    return fail(SFKV_EINVAL, "the handle was set up on device " + std::to_string(dev) + ", device " +
+                                 std::to_string(cur) + " is current");
+  return SFKV_OK;
+}
+
 sfkv_status check_frame(const sfkv_cache *c, const void *k, const void *v, sfkv_dtype dtype,
                         int32_t n) {
   if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (check_device(c->device) != SFKV_OK) return SFKV_EINVAL;
   if (!k || !v) return fail(SFKV_EINVAL, "k and v must be device pointers");
   if (!aligned(k, 16) || !aligned(v, 16)) return fail(SFKV_EINVAL, "k and v must be 16-byte aligned");
   if (dtype != SFKV_BF16 && dtype != SFKV_FP32) return fail(SFKV_EINVAL, "dtype must be SFKV_BF16 or SFKV_FP32");
@@ -107,11 +123,6 @@ sfkv_status check_frame(const sfkv_cache *c, const void *k, const void *v, sfkv_
 
 // Compute units of the current device (the attention grid is planned for two
 // workgroups per CU); 256 if the runtime cannot say.
-int current_device() {
-  int dev = -1;
-  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
-}
-
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -413,6 +424,7 @@ static sfkv_status attend_planes(const sfkv_cache_cfg &cfg, int cus, const sfkv_
 sfkv_status sfkv_attend(sfkv_cache *c, const void *q, sfkv_dtype dtype, int32_t n_q, float *out,
                         void *workspace, size_t workspace_bytes, void *stream) {
   if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (check_device(c->device) != SFKV_OK) return SFKV_EINVAL;
   if (c->last_n == 0) return fail(SFKV_ESTATE, "attend before any cache_write");
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last cache_write");
   return attend_planes(c->cfg, c->cus, c->rope, c->base, n_valid_of(c), c->last_pos0, q, dtype, n_q, out,
@@ -511,6 +523,7 @@ static sfkv_status rebase_caches(sfkv_cache *const *caches, const int64_t *delta
 
 sfkv_status sfkv_rebase_positions(sfkv_cache *c, int64_t delta, void *stream) {
   if (!c) return fail(SFKV_EINVAL, "cache is NULL");
+  if (check_device(c->device) != SFKV_OK) return SFKV_EINVAL;
   if (delta < 0 || delta > c->next_pos) return fail(SFKV_ERANGE, "delta must be in [0, next_pos]");
   return rebase_caches(&c, &delta, 1, stream);
 }
@@ -574,6 +587,7 @@ struct sfkv_linear {
   int32_t last_n;
   int cur;               // window holding the current tokens
   int cus;               // compute units of the device the cache was set up on
+  int device;            // that device's index
   bool calibrated;
 };
 
@@ -598,6 +612,7 @@ LinearLayout linear_layout_of(const sfkv_cache_cfg &c, sfkv_dtype dtype) {
 
 sfkv_status check_linear_frame(const sfkv_linear *c, const void *k, const void *v, int32_t n) {
   if (!c) return fail(SFKV_EINVAL, "linear cache is NULL");
+  if (check_device(c->device) != SFKV_OK) return SFKV_EINVAL;
   if (!k || !v) return fail(SFKV_EINVAL, "k and v must be device pointers");
   if (!aligned(k, 16) || !aligned(v, 16)) return fail(SFKV_EINVAL, "k and v must be 16-byte aligned");
   if (n < 1 || n > c->cfg.max_new_tokens) return fail(SFKV_EINVAL, "n_tokens must be in [1, max_new_tokens]");
@@ -643,6 +658,7 @@ sfkv_status sfkv_linear_init(const sfkv_cache_cfg *cfg, const sfkv_rope *rope, s
   c->last_n = 0;
   c->cur = 0;
   c->cus = device_cus();
+  c->device = current_device();
   c->calibrated = false;
   *out = c;
   return ok();
@@ -727,6 +743,7 @@ size_t sfkv_linear_workspace_bytes(const sfkv_linear *c) {
 sfkv_status sfkv_linear_attend(sfkv_linear *c, const void *q, int32_t n_q, float *out, void *workspace,
                                size_t workspace_bytes, void *stream) {
   if (!c) return fail(SFKV_EINVAL, "linear cache is NULL");
+  if (check_device(c->device) != SFKV_OK) return SFKV_EINVAL;
   if (c->last_n == 0) return fail(SFKV_ESTATE, "linear_attend before any linear_write");
   if (n_q != c->last_n) return fail(SFKV_EINVAL, "n_q must equal the n_tokens of the last linear_write");
   return attend_planes(c->cfg, c->cus, c->rope, c->base, c->m, c->m - c->last_n, q, c->dtype, n_q, out,
