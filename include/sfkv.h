@@ -111,6 +111,9 @@ typedef struct {
  * for positions 0 .. max_position (inclusive), [max_position + 1][head_dim/2].
  * Built on the host once and uploaded; sfkv_rope_init synchronises `stream`
  * before returning (set-up only, never in the per-step path).
+ * Errors: EINVAL (head_dim not 64 or 128, max_position outside [1, 2^26], base
+ *         not finite or not above 1, dev_mem NULL, unaligned or smaller than
+ *         sfkv_rope_bytes(), no host memory for the table), EHIP (upload).
  * Source: "Do It Once, at Write Time" (RoPE applied once at write). */
 size_t sfkv_rope_bytes(int32_t head_dim, int32_t max_position);
 sfkv_status sfkv_rope_init(double base, int32_t head_dim, int32_t max_position,

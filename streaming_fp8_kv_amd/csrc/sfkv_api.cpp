@@ -202,9 +202,15 @@ sfkv_status sfkv_rope_init(double base, int32_t head_dim, int32_t max_position, 
   // theta_i = base^((-2 i) / d); angle = p * theta_i in fp64; cos and sin from
   // the C library, each rounded once to fp32.
   const int half = head_dim / 2;
-  std::vector<double> theta(half);
+  std::vector<double> theta;
+  std::vector<sfkv::RopePair> host;
+  try {   // no C++ exception may leave a C entry point
+    theta.resize(half);
+    host.resize(static_cast<size_t>(max_position + 1) * half);
+  } catch (const std::bad_alloc &) {
+    return fail(SFKV_EINVAL, "out of host memory for the rope table");
+  }
   for (int i = 0; i < half; ++i) theta[i] = std::pow(base, (-2.0 * static_cast<double>(i)) / static_cast<double>(head_dim));
-  std::vector<sfkv::RopePair> host(static_cast<size_t>(max_position + 1) * half);
   for (int64_t p = 0; p <= max_position; ++p) {
     for (int i = 0; i < half; ++i) {
       const double ang = static_cast<double>(p) * theta[i];
@@ -484,7 +490,12 @@ static void rebased(sfkv_cache *c, int64_t delta) {
 // cache's host state once its launch has been enqueued.
 static sfkv_status rebase_caches(sfkv_cache *const *caches, const int64_t *deltas, int32_t count,
                                  void *stream) {
-  std::vector<char> done(static_cast<size_t>(count), 0);
+  std::vector<char> done;
+  try {
+    done.assign(static_cast<size_t>(count), 0);
+  } catch (const std::bad_alloc &) {
+    return fail(SFKV_EINVAL, "out of host memory");
+  }
   for (int32_t i = 0; i < count; ++i) {
     if (done[i]) continue;
     if (deltas[i] == 0 || n_valid_of(caches[i]) == 0) {   // nothing on the device to move
@@ -542,7 +553,12 @@ sfkv_status sfkv_rebase_positions_many(sfkv_cache *const *caches, const int64_t 
   for (int32_t i = 0; i < count; ++i)
     if (caches[i]->device != dev)
       return fail(SFKV_EINVAL, "caches[" + std::to_string(i) + "] was set up on another device than the current one");
-  std::vector<const sfkv_cache *> sorted(caches, caches + count);
+  std::vector<const sfkv_cache *> sorted;
+  try {
+    sorted.assign(caches, caches + count);
+  } catch (const std::bad_alloc &) {
+    return fail(SFKV_EINVAL, "out of host memory");
+  }
   std::sort(sorted.begin(), sorted.end());
   if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
     return fail(SFKV_EINVAL, "a cache appears more than once");
