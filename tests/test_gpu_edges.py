@@ -107,3 +107,44 @@ def test_positions_up_to_the_table_end(sfkv, storage):
     m.write(k, v)
     m.check_cache("write after reset")
     m.check_attend(q, tag="write after reset")
+
+
+@pytest.mark.parametrize("storage", ["fp8", "bf16"])
+def test_one_key_dominates(sfkv, storage):
+    """Small keys everywhere except one token per head whose key points along a
+    unit direction the frame's queries share, scaled so that, fully aligned,
+    its score is about 40 log2 units above the rest: for the queries it lines up
+    with, the running maximum jumps far past its reference and every other
+    weight underflows in fp16 (a one-hot output), for the others it sits
+    anywhere between; key ranges whose maxima differ by tens of units are
+    merged. Calibrated on a frame that holds the large key with headroom, so
+    the E4M3 cache does not clip it. Every call against the oracle; a reset in
+    between."""
+    heads, d, cap, n = 2, 128, 512, 96
+    shape = W.CacheShape(heads, d, cap, n, max_position=4096)
+    spec = W.WorkloadSpec(name="one_key", shape=shape, seed=97, dtype=torch.float32, dist="normal",
+                          sigma_q=None, sigma_kv=None, steps=7)
+    say(f"case one dominating key {storage}")
+    m = Mirror(sfkv, sfkv.Rope(d, shape.max_position), spec, storage=storage)
+    fs = W.FrameStream(spec)
+    g = torch.Generator().manual_seed(98)
+    u = torch.randn(heads, d, generator=g)
+    u = u / u.norm(dim=1, keepdim=True)
+    big = 17.7                              # |q||k| = 313: 40 log2 units once divided by sqrt(d), times log2(e)
+    for step in range(spec.steps):
+        q, k, v = fs.frame()
+        k *= 0.05
+        q = big * u[None].expand(n, heads, d).contiguous() + 0.05 * q
+        if step == 0:
+            cal = k.clone()
+            cal[0] = 1.5 * big * u
+            m.calibrate(cal, v)
+        if step == 2:
+            k[37] = big * u                 # the dominating key, one token of the third frame
+            v[37] = torch.linspace(-3.0, 3.0, d)
+        if step == 5:
+            m.rebase(m.ora.next_pos)
+            m.check_cache("after reset")
+        m.write(k, v)
+        m.check_cache(f"step {step}")
+        m.check_attend(q, tag=f"step {step}")
