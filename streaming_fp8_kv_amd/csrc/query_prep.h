@@ -15,17 +15,19 @@ namespace qprep {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bhalf2_t __attribute__((ext_vector_type(2)));
 typedef float fl2_t __attribute__((ext_vector_type(2)));
+typedef short sh2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2eQ = 1.4426950408889634f;
 
 // Smallest e with m * 2^-e <= 448, from the exact binary exponent of m
-// (448 = 0.875 * 2^9); clamped to the E8M0 range.
+// (448 = 0.875 * 2^9); clamped to [-126, 127], so 2^e is a normal float and
+// 127 + e a valid E8M0 byte.
 __device__ inline int block_exponent(float m) {
   if (!(m > 0.0f)) return 0;
   int E;
   float f = frexpf(m, &E);   // m = f * 2^E, f in [0.5, 1)
   int e = (f <= 0.875f) ? E - 9 : E - 8;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
 }
 
 // 8 consecutive query elements (bf16 or fp32) as fp32.
@@ -104,20 +106,24 @@ __device__ inline void prep_e4m3(const AttendLaunch &a, unsigned idx) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
     const int e = block_exponent(quad_max(m));
+    // gfx950's scaled conversions divide by the scale operand on the way to
+    // E4M3 and multiply by it on the way back: with 2^e they equal scaling by
+    // 2^-e (exact) then rounding, and decoding then scaling by 2^e (exact)
+    const float sc = __int_as_float((127 + e) << 23);
     int w[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j], -e), ldexpf(x[4 * j + 1], -e), 0, false);
-      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j + 2], -e), ldexpf(x[4 * j + 3], -e), lo, true);
+      const sh2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((sh2_t){0, 0}, x[4 * j], x[4 * j + 1], sc, false);
+      w[j] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[4 * j + 2], x[4 * j + 3], sc, true));
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);
-      x[4 * j] -= ldexpf(lo[0], e);
-      x[4 * j + 1] -= ldexpf(lo[1], e);
-      x[4 * j + 2] -= ldexpf(hi[0], e);
-      x[4 * j + 3] -= ldexpf(hi[1], e);
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], sc, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], sc, true);
+      x[4 * j] -= lo[0];
+      x[4 * j + 1] -= lo[1];
+      x[4 * j + 2] -= hi[0];
+      x[4 * j + 3] -= hi[1];
     }
     *reinterpret_cast<uint2 *>(a.qterm + (static_cast<size_t>(qh) * 3 + t) * D + 32 * b + 8 * g) =
         uint2{static_cast<uint32_t>(w[0]), static_cast<uint32_t>(w[1])};
