@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kCalibrateThreads) void calibrate_kernel(CalibrateL
   if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < (blockDim.x >> 6); ++w) m = fmaxf(m, partial[w]);
+    for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) m = fmaxf(m, partial[w]);
     m = fmaxf(m, partial[0]);
     float scale = 1.0f, inv = 1.0f;
     if (m > 0.0f && a.storage == kBF16) {
