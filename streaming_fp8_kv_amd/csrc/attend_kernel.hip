@@ -203,7 +203,7 @@ __global__ __launch_bounds__(attend_threads(ST), ST == kE4M3 ? 2 : 1) void atten
   const int NB = (n_pairs - X) * slo, NS = X * (slo + 1);
   const int xcd = blockIdx.x & 7, jl = blockIdx.x >> 3;
   const int b0 = NB * xcd / 8, nb = NB * (xcd + 1) / 8 - b0;
-  const int s0 = NS * xcd / 8, ns = NS * (xcd + 1) / 8 - s0;
+  const int sm0 = NS * xcd / 8, ns = NS * (xcd + 1) / 8 - sm0;
   int pair, split, nsplit;
   if (jl < nb) {
     const int b = b0 + jl;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(attend_threads(ST), ST == kE4M3 ? 2 : 1) void atten
     nsplit = slo;
   } else {
     if (jl - nb >= ns) return;
-    const int sm = s0 + jl - nb;
+    const int sm = sm0 + jl - nb;
     pair = sm / (slo + 1);
     split = sm % (slo + 1);
     nsplit = slo + 1;
