@@ -10,7 +10,7 @@ import torch
 from oracle import e4m3
 from oracle.cache import RingCache as OracleCache
 from streaming_fp8_kv_amd import workloads as W
-from tests.gpu_helpers import Mirror, say
+from tests.gpu_helpers import say
 
 pytestmark = pytest.mark.gpu
 

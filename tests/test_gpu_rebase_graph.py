@@ -24,7 +24,7 @@ import torch
 from oracle.cache import RingCache as OracleCache, softmax_attention
 from oracle import bf16 as obf16
 from streaming_fp8_kv_amd import workloads as W
-from tests.gpu_helpers import (A_MAX, B_MEAN, Mirror, attention_error, bf16_staging_factors, say,
+from tests.gpu_helpers import (A_MAX, B_MEAN, Mirror, attention_error, say,
                                spread_rows)
 
 pytestmark = pytest.mark.gpu

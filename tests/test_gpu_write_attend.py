@@ -6,7 +6,6 @@ must equal those of cache_write followed by attend bit for bit, for both
 storages, both head dims and both input dtypes. The production-shape case is
 also checked against the oracle.
 """
-import numpy as np
 import pytest
 import torch
 

@@ -6,9 +6,7 @@ cache on the same GPU after them (the static scratch keeps the last call's
 contents and nothing in it may be assumed zero); a configuration needing more
 scratch than the maximum is rejected with the state unchanged; and no device
 memory is allocated by the calls."""
-import ctypes
 
-import numpy as np
 import pytest
 import torch
 
